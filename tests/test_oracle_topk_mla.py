@@ -1,0 +1,255 @@
+"""Pins of the oracle's top-k selection and sparse MLA.
+
+Top-k ("一文讀懂DeepSeek-V3.2核心技術DSA", "DSA 的四步工作流程", the top-k step): the k best
+positions per query, and every position when the context is not longer than k; ties go to the
+lower position.  Checked against closed forms, brute force over all subsets, and numpy's lexsort.
+
+Sparse MLA (same page, the sparse-MLA step; "DeepSeek-V3.2加速技术详解" section 3.1, MQA form):
+softmax attention of each head over the selected 576-dim latent rows, values = first 512 dims.
+Checked against closed forms and torch's scaled_dot_product_attention in float64 (the
+short-context case, where sparse attention must equal dense causal attention).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _sets(idx):
+    return [sorted(int(v) for v in row if v >= 0) for row in idx]
+
+
+# ---------------------------------------------------------------------------------------------
+# top-k
+
+def test_topk_monotone_scores_select_last_k():
+    n, k = 50, 7
+    s = np.arange(n, dtype=np.float64)[None]
+    got = oracle.topk(s, np.array([n], np.int32), k)
+    assert got[0].tolist() == list(range(n - 1, n - 1 - k, -1))
+
+
+def test_topk_all_equal_selects_lowest_positions():
+    n, k = 40, 9
+    got = oracle.topk(np.full((1, n), 3.5), np.array([n], np.int32), k)
+    assert got[0].tolist() == list(range(k))
+
+
+def test_topk_short_context_selects_everything():
+    k = 16
+    s = np.random.default_rng(0).standard_normal((3, 20))
+    q_len = np.array([1, 16, 5], np.int32)
+    got = oracle.topk(s, q_len, k)
+    for r in range(3):
+        assert got[r, :q_len[r]].tolist() == list(range(q_len[r]))
+        assert np.all(got[r, q_len[r]:] == -1)
+
+
+def test_topk_signed_zeros_tie():
+    """+0 and -0 are the same real number: ties among them go to the lower position."""
+    row = np.array([-0.0, 0.0, -0.0, 1.0, 0.0, -1.0, -0.0])
+    got = oracle.topk(row[None], np.array([7], np.int32), 3)
+    assert sorted(got[0].tolist()) == [0, 1, 3]
+
+
+def test_topk_matches_lexsort_with_forced_ties():
+    rng = np.random.default_rng(1)
+    R, n, k = 20, 300, 37
+    s = rng.integers(0, 12, size=(R, n)).astype(np.float64)     # many ties
+    s[::3] = rng.standard_normal((len(s[::3]), n))
+    q_len = rng.integers(k + 1, n + 1, size=R).astype(np.int32)
+    got = oracle.topk(s, q_len, k)
+    for r in range(R):
+        m = q_len[r]
+        order = np.lexsort((np.arange(m), -s[r, :m]))           # by -score, then position
+        assert got[r].tolist() == order[:k].tolist()
+
+
+def test_topk_brute_force_subsets():
+    """The selection is the unique k-subset X with: for x in X, y not in X, s[x] > s[y] or
+    (s[x] == s[y] and x < y).  Enumerate every subset of tiny rows."""
+    rng = np.random.default_rng(2)
+    for trial in range(60):
+        n = int(rng.integers(2, 9))
+        k = int(rng.integers(1, n))
+        row = rng.integers(-2, 3, size=n).astype(np.float64)
+        ok = []
+        for X in itertools.combinations(range(n), k):
+            Xs = set(X)
+            if all(row[x] > row[y] or (row[x] == row[y] and x < y)
+                   for x in Xs for y in range(n) if y not in Xs):
+                ok.append(sorted(X))
+        assert len(ok) == 1
+        got = oracle.topk(row[None], np.array([n], np.int32), k)
+        assert sorted(got[0].tolist()) == ok[0]
+
+
+def test_topk_ignores_positions_beyond_context():
+    row = np.array([[1.0, 2.0, 3.0, 9.0, 9.0]])
+    got = oracle.topk(row, np.array([4], np.int32), 2, rows=np.array([0], np.int32))
+    assert sorted(got[0].tolist()) == [2, 3]
+    got = oracle.topk(row, np.array([3], np.int32), 2)
+    assert sorted(got[0].tolist()) == [1, 2]
+
+
+# ---------------------------------------------------------------------------------------------
+# sparse MLA
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _val(bits):
+    return oracle.decode(bits, "bf16")
+
+
+def _mla_inputs(rng, T, H, n, q_sigma=1.0 / 24, Dqk=576):
+    q = _bf16(rng.standard_normal((T, H, Dqk)) * q_sigma)
+    lat = _bf16(rng.standard_normal((n, Dqk)) / 24)
+    return q, lat
+
+
+def test_single_index_returns_that_row():
+    rng = np.random.default_rng(3)
+    q, lat = _mla_inputs(rng, 2, 4, 30)
+    idx = np.full((2, 8), -1, np.int32); idx[0, 3] = 17; idx[1, 0] = 2
+    out, lse = oracle.sparse_mla(q, lat, np.zeros(2, np.int32), np.array([30, 30], np.int32), idx,
+                                 seq_stride=30, softmax_scale=0.7)
+    L = _val(lat); Q = _val(q)
+    for t, s in ((0, 17), (1, 2)):
+        np.testing.assert_array_equal(out[t], np.broadcast_to(L[s, :512], (4, 512)))
+        np.testing.assert_allclose(lse[t], 0.7 * (Q[t] @ L[s]), rtol=1e-14)
+
+
+def test_zero_query_gives_mean_of_selected_values():
+    rng = np.random.default_rng(4)
+    _, lat = _mla_inputs(rng, 1, 2, 40)
+    q = np.zeros((1, 2, 576), np.uint16)
+    sel = [1, 5, 6, 22, 39]
+    idx = np.array([sel + [-1] * 3], np.int32)
+    out, lse = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([40], np.int32), idx, seq_stride=40)
+    mean = _val(lat)[sel, :512].mean(axis=0)
+    np.testing.assert_allclose(out[0, 0], mean, rtol=1e-13, atol=1e-18)
+    np.testing.assert_allclose(lse[0], np.log(len(sel)), rtol=1e-14)
+
+
+@pytest.mark.parametrize("q_sigma", [1.0 / 24, 72.0])
+def test_short_context_equals_dense_causal_attention_sdpa(q_sigma):
+    """Context <= k selects every past token, so DSA is dense causal attention: compare with
+    torch.nn.functional.scaled_dot_product_attention in float64 (MQA: one shared K/V head)."""
+    rng = np.random.default_rng(5)
+    L, H, k = 70, 4, 128
+    q, lat = _mla_inputs(rng, L, H, L, q_sigma=q_sigma)
+    q_len = np.arange(1, L + 1, dtype=np.int32)
+    idx = oracle.topk(np.zeros((L, L)), q_len, k)       # n <= k: all positions
+    out, lse = oracle.sparse_mla(q, lat, np.zeros(L, np.int32), q_len, idx, seq_stride=L,
+                                 softmax_scale=1 / 24)
+    Q = torch.from_numpy(_val(q)).permute(1, 0, 2)               # [H, L, 576]
+    Lt = torch.from_numpy(_val(lat))
+    K = Lt[None].expand(H, L, 576)
+    V = Lt[None, :, :512].expand(H, L, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=1 / 24)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-14)
+    # lse against an independent logsumexp
+    z = (Q @ K.transpose(1, 2)) / 24
+    z = z.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=-1).T.numpy(), rtol=1e-12)
+
+
+def test_index_order_and_padding_do_not_matter():
+    rng = np.random.default_rng(6)
+    q, lat = _mla_inputs(rng, 1, 3, 64, q_sigma=1.0)
+    sel = rng.choice(64, size=20, replace=False).astype(np.int32)
+    a = np.full((1, 32), -1, np.int32); a[0, :20] = sel
+    b = np.full((1, 32), -1, np.int32); b[0, 12:] = sel[::-1]
+    c = np.full((1, 32), -1, np.int32); c[0, :20] = sel; c[0, 20:24] = [64, 70, 1000, -5]  # out of range
+    args = dict(seq_stride=64, softmax_scale=1 / 24)
+    o1, l1 = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([64], np.int32), a, **args)
+    o2, l2 = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([64], np.int32), b, **args)
+    o3, l3 = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([64], np.int32), c, **args)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-17)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+    np.testing.assert_array_equal(o1, o3)
+
+
+def test_no_selection_gives_zero_and_neg_inf():
+    rng = np.random.default_rng(7)
+    q, lat = _mla_inputs(rng, 1, 2, 8)
+    out, lse = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([8], np.int32),
+                                 np.full((1, 4), -1, np.int32), seq_stride=8)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_sparse_equals_dense_with_minus_inf_mask():
+    """Attention restricted to a subset equals dense softmax whose excluded logits are -inf."""
+    rng = np.random.default_rng(8)
+    n, H = 90, 2
+    q, lat = _mla_inputs(rng, 1, H, n, q_sigma=2.0)
+    sel = np.sort(rng.choice(n, size=33, replace=False)).astype(np.int32)
+    out, _ = oracle.sparse_mla(q, lat, np.zeros(1, np.int32), np.array([n], np.int32), sel[None],
+                               seq_stride=n, softmax_scale=1 / 24)
+    Q = torch.from_numpy(_val(q)[0]); Lt = torch.from_numpy(_val(lat))
+    mask = torch.full((H, n), float("-inf"), dtype=torch.float64); mask[:, sel] = 0
+    p = torch.softmax(Q @ Lt.T / 24 + mask, dim=-1)
+    np.testing.assert_allclose(out[0], (p @ Lt[:, :512]).numpy(), rtol=1e-11, atol=1e-16)
+
+
+def test_paged_latent_matches_contiguous():
+    rng = np.random.default_rng(9)
+    B, n, H, page = 2, 130, 2, 64
+    q, _ = _mla_inputs(rng, B, H, 1)
+    lat = _bf16(rng.standard_normal((B, n, 576)) / 24)
+    idx = np.stack([rng.choice(n, 40, replace=False) for _ in range(B)]).astype(np.int32)
+    q_seq = np.arange(B, dtype=np.int32); q_len = np.full(B, n, np.int32)
+    oc, lc = oracle.sparse_mla(q, lat.reshape(B * n, 576), q_seq, q_len, idx, seq_stride=n)
+    ppb = 3
+    perm = rng.permutation(B * ppb)
+    pool = np.zeros((B * ppb * page, 576), np.uint16); pt = np.zeros((B, ppb), np.int32)
+    for b in range(B):
+        for lp in range(ppb):
+            ph = perm[b * ppb + lp]; pt[b, lp] = ph
+            rows = lat[b, lp * page:(lp + 1) * page]
+            pool[ph * page:ph * page + len(rows)] = rows
+    op, lp_ = oracle.sparse_mla(q, pool, q_seq, q_len, idx, page_table=pt, page_size=page)
+    np.testing.assert_array_equal(op, oc)
+    np.testing.assert_array_equal(lp_, lc)
+
+
+def test_forward_short_context_is_full_attention():
+    """Prefill with k >= L: forward == dense causal attention for every query."""
+    rng = np.random.default_rng(10)
+    L, H, HI = 48, 2, 4
+    q_idx = rng.standard_normal((L, HI, 128)).astype(np.float32)
+    k_idx = rng.standard_normal((L, 128)).astype(np.float32)
+    w = rng.uniform(0, 1, (L, HI)).astype(np.float32)
+    q, lat = _mla_inputs(rng, L, H, L)
+    q_len = np.arange(1, L + 1, dtype=np.int32)
+    idx, out, lse = oracle.forward(q_idx, "f32", None, w, k_idx, "f32", None, q, lat,
+                                   np.zeros(L, np.int32), q_len, 64, seq_stride=L, softmax_scale=1 / 24)
+    Q = torch.from_numpy(_val(q)).permute(1, 0, 2); Lt = torch.from_numpy(_val(lat))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, Lt[None].expand(H, L, 576),
+                                                           Lt[None, :, :512].expand(H, L, 512),
+                                                           is_causal=True, scale=1 / 24)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_forward_selects_indexer_topk_when_context_exceeds_k():
+    rng = np.random.default_rng(11)
+    L, H, HI, k = 40, 2, 4, 8
+    q_idx = rng.standard_normal((L, HI, 128)).astype(np.float32)
+    k_idx = rng.standard_normal((L, 128)).astype(np.float32)
+    w = rng.uniform(0, 1, (L, HI)).astype(np.float32)
+    q, lat = _mla_inputs(rng, L, H, L)
+    q_len = np.arange(1, L + 1, dtype=np.int32); q_seq = np.zeros(L, np.int32)
+    idx, out, lse = oracle.forward(q_idx, "f32", None, w, k_idx, "f32", None, q, lat, q_seq, q_len, k,
+                                   seq_stride=L)
+    S = oracle.indexer(q_idx, "f32", None, w, k_idx, "f32", None, q_seq, q_len, seq_stride=L, ld=L)
+    for t in range(L):
+        n = q_len[t]
+        want = list(range(n)) if n <= k else np.lexsort((np.arange(n), -S[t, :n]))[:k].tolist()
+        assert sorted(idx[t][idx[t] >= 0].tolist()) == sorted(want)
+    o2, l2 = oracle.sparse_mla(q, lat, q_seq, q_len, idx, seq_stride=L)
+    np.testing.assert_array_equal(out, o2)
