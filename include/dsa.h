@@ -1,0 +1,154 @@
+/*
+ * dsa.h -- C ABI of libdsa, the DeepSeek Sparse Attention (DSA) hot path for AMD MI355X (gfx950).
+ *
+ * The path has three steps, each with its own entry point, and one entry point that runs all three:
+ *
+ *   dsa_indexer_scores  the lightning indexer: for every query token t and every visible past token s
+ *                       S[t,s] = scale * k_scale[s] * sum_j w'[t,j] * max(0, q[t,j,:] . k[s,:]),
+ *                       w'[t,j] = weights[t,j] * q_scale[t,j]
+ *                       (page "一文讀懂DeepSeek-V3.2核心技術DSA", section "DSA 的四步工作流程", the
+ *                       indexer-scoring step: Q.K over a small 128-dim key cache, mask and scale, then
+ *                       the per-head weights; page "DeepSeek 稀疏注意力路线（V3 / V3.2 / V4）",
+ *                       section "两阶段流程", item 1: ReLU-type activation, FP8, heads aggregated).
+ *   dsa_topk            per query, the k positions with the largest scores, ties to the lower position;
+ *                       every position when the context has at most k tokens (same page, top-k step,
+ *                       and its special case that a short context selects everything).
+ *   dsa_sparse_mla      attention of every query head over the selected 576-dim latent rows only, in
+ *                       MQA form: keys are the whole 576-dim row (512 latent + 64 decoupled-RoPE dims),
+ *                       values its first 512 dims (same page, the sparse-MLA step and the 512-dim key
+ *                       cache of the second component; page "DeepSeek-V3.2加速技术详解", section 3.1
+ *                       "MHA版MLA VS MQA版MLA": the attention runs on the shared latent vectors and the
+ *                       value up-projection is applied afterwards, outside this library).
+ *   dsa_forward         indexer -> top-k -> sparse MLA; queries whose context is at most k skip the
+ *                       indexer and take every position.
+ *
+ * Conventions shared by every call
+ *   - All array pointers are DEVICE pointers unless marked "host"; the structs themselves live in host
+ *     memory and are read during the call only.  The caller owns every buffer; the library allocates
+ *     no device memory.  Scratch space comes from the caller's `workspace`, sized by
+ *     dsa_workspace_size().
+ *   - Work is enqueued on `stream` and the call returns without waiting for it.  Buffers must stay
+ *     valid until the stream has run the work.
+ *   - Argument errors are reported synchronously, before anything is launched, as DSA_ERR_INVALID_ARG
+ *     or DSA_ERR_UNSUPPORTED; a failed launch is DSA_ERR_HIP.  dsa_last_error() then holds a
+ *     per-thread message.  No C++ exception crosses this interface.
+ *   - The library keeps no global mutable state apart from that per-thread message.
+ *   - Results are deterministic: the same inputs give bitwise identical outputs.
+ *   - Token positions are LOGICAL positions 0..n-1 within a sequence, independent of paging.
+ *   - Device-side index data (q_len, q_seq, cu_q, page tables, selected indices) is bounds-checked
+ *     where it is used: a length above max_len is read as max_len, a query whose sequence number is out
+ *     of range is skipped, a selected index outside [0, n_t) is skipped, and a physical page number
+ *     outside [0, num_pages) reads as an all-zero row.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,   /* a pointer, size or layout argument is wrong */
+    DSA_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than dsa_workspace_size() */
+    DSA_ERR_HIP = 4            /* the HIP runtime reported an error */
+} dsa_status;
+
+typedef enum {
+    DSA_F32 = 0,
+    DSA_BF16 = 1,
+    DSA_FP8_E4M3 = 2           /* OCP e4m3fn: bias 7, no infinities, max 448 */
+} dsa_dtype;
+
+/* A per-token cache: either contiguous, token s of sequence b at row b*seq_stride + s, or paged,
+ * token s of sequence b at row page_table[b*page_table_stride + s/page_size]*page_size + s%page_size. */
+typedef struct {
+    const void* data;            /* device, [num_rows][dim] elements of `dtype` */
+    const float* scale;          /* device, one float per row (fp8 only), or NULL for all-ones */
+    int32_t dtype;               /* dsa_dtype */
+    int32_t dim;                 /* elements per row: 128 (indexer keys) or 576 (latent) */
+    int64_t num_rows;            /* rows addressable through `data` (used to check the layout) */
+    int64_t seq_stride;          /* contiguous layout: rows between consecutive sequences */
+    const int32_t* page_table;   /* device [num_seqs][page_table_stride], or NULL for contiguous */
+    int32_t page_table_stride;   /* entries per sequence in page_table */
+    int32_t page_size;           /* tokens per page (paged layout) */
+} dsa_cache;
+
+/* A batch of query tokens grouped by sequence (queries of a sequence are consecutive). */
+typedef struct {
+    int32_t num_queries;         /* T */
+    int32_t num_seqs;            /* B */
+    const int32_t* cu_q;         /* device [B+1]: queries of sequence b are cu_q[b] .. cu_q[b+1]-1 */
+    const int32_t* q_seq;        /* device [T]: sequence of each query */
+    const int32_t* q_len;        /* device [T]: n_t, query t sees its sequence's tokens 0..n_t-1
+                                    (causal; a token sees itself, so in prefill n_t = position + 1) */
+    int32_t max_len;             /* host: an upper bound of every n_t (sizes grids and score rows) */
+    int32_t max_q;               /* host: an upper bound of the queries of one sequence */
+} dsa_batch;
+
+/* Lightning-indexer scores.
+ *   q        [T][n_heads][head_dim] in q_dtype (F32, BF16 or FP8_E4M3)
+ *   q_scale  [T][n_heads] floats (one per 128-wide fp8 row) or NULL for all-ones; must be >= 0
+ *   weights  [T][n_heads] floats (any sign)
+ *   k_cache  the 128-dim indexer key cache, dtype F32, BF16 or FP8_E4M3 (fp8 scales >= 0)
+ *   scale    scalar multiplier of every score
+ *   scores   [T][ld] floats, ld >= max_len: entry s of row t is written for s < n_t; entries at
+ *            s >= n_t are left untouched (they are masked out of the selection)
+ * head_dim must be 128; q_dtype must equal k_cache->dtype. */
+dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
+                              int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache,
+                              const dsa_batch* batch, float scale, float* scores, int64_t ld,
+                              hipStream_t stream);
+
+/* Top-k positions per query from the score rows.
+ *   scores   [T][ld] floats; only entries s < n_t of row t are read
+ *   indices  [T][k] int32: the selected positions in ascending order, then -1 padding (n_t < k)
+ * Scores are compared as real numbers (+0 == -0); equal scores go to the lower position.  NaN scores
+ * are not supported.  workspace may be NULL (this operation needs none). */
+dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse MLA in MQA form over the selected latent rows.
+ *   q        [T][n_heads][d_qk] bf16 (d_qk = 576)
+ *   latent   the latent cache, BF16, dim 576; values are the first d_v = 512 dims of each row
+ *   indices  [T][k] int32 logical positions; entries outside [0, n_t) (e.g. -1 padding) are skipped;
+ *            valid entries must be distinct
+ *   out      [T][n_heads][d_v] bf16: sum_j softmax_j(softmax_scale * q.c_j) * c_j[:d_v]
+ *   lse      [T][n_heads] floats (natural-log log-sum-exp of the scaled logits) or NULL
+ * A query with no valid index gets out = 0 and lse = -inf.  1 <= n_heads <= 128. */
+dsa_status dsa_sparse_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
+                          const dsa_batch* batch, const int32_t* indices, int32_t k, float softmax_scale,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Indexer -> top-k -> sparse MLA for one batch (arguments as in the three calls above).
+ * indices_out may be NULL (the selection then lives in the workspace). */
+dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale,
+                       const float* weights, int32_t idx_heads, const dsa_cache* k_cache, float idx_scale,
+                       int32_t k,
+                       const void* q, int32_t n_heads, const dsa_cache* latent, float softmax_scale,
+                       const dsa_batch* batch, int32_t* indices_out, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Operations for dsa_workspace_size. */
+enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
+
+/* Bytes of workspace the operation needs for this batch (0 if none).  For DSA_OP_FORWARD, `k` is the
+ * top-k size and indices_out is assumed NULL (the worst case). */
+size_t dsa_workspace_size(int32_t op, const dsa_batch* batch, int32_t k, int32_t n_heads, int32_t d_v);
+
+const char* dsa_status_string(dsa_status s);
+const char* dsa_last_error(void);   /* message of this thread's last failed call ("" if none) */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,246 @@
+// api.hip -- the libdsa C ABI: argument checks, workspace layout, kernel launches.
+//
+// Every entry point validates its arguments on the host and returns before launching anything when
+// they are wrong.  Kernels are enqueued on the caller's stream; nothing here waits for the device.
+#include <cstdio>
+#include <cstring>
+#include <cstdarg>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DSA_OK;
+    return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxK = 65536;
+constexpr int kMaxHeads = 128;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t score_ld(const dsa_batch* b) { return ((int64_t)b->max_len + 63) & ~(int64_t)63; }
+
+dsa_status check_batch(const dsa_batch* b) {
+    if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+    if (b->num_queries < 0 || b->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "batch: num_queries < 0 or num_seqs < 1");
+    if (b->max_len < 0) return fail(DSA_ERR_INVALID_ARG, "batch: max_len < 0");
+    if (b->num_queries > 0) {
+        if (!b->cu_q || !b->q_seq || !b->q_len) return fail(DSA_ERR_INVALID_ARG, "batch: cu_q / q_seq / q_len is NULL");
+        if (b->max_q < 1 || b->max_q > b->num_queries)
+            return fail(DSA_ERR_INVALID_ARG, "batch: max_q must be in [1, num_queries]");
+    }
+    return DSA_OK;
+}
+
+dsa_status check_cache(const dsa_cache* c, const dsa_batch* b, int dim, const char* name) {
+    if (!c) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s: data is NULL", name);
+    if (c->dim != dim) return fail(DSA_ERR_UNSUPPORTED, "%s: dim %d, expected %d", name, c->dim, dim);
+    if (c->dtype != DSA_F32 && c->dtype != DSA_BF16 && c->dtype != DSA_FP8_E4M3)
+        return fail(DSA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, c->dtype);
+    if (c->num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_rows < 0", name);
+    if (c->page_table) {
+        if (c->page_size < 1) return fail(DSA_ERR_INVALID_ARG, "%s: page_size < 1", name);
+        const int64_t need = ((int64_t)b->max_len + c->page_size - 1) / c->page_size;
+        if (c->page_table_stride < need)
+            return fail(DSA_ERR_INVALID_ARG, "%s: page_table_stride %d < %lld pages for max_len", name,
+                        c->page_table_stride, (long long)need);
+        if (c->num_rows < c->page_size) return fail(DSA_ERR_INVALID_ARG, "%s: fewer rows than one page", name);
+    } else {
+        if (c->seq_stride < b->max_len)
+            return fail(DSA_ERR_INVALID_ARG, "%s: seq_stride %lld < max_len %d", name, (long long)c->seq_stride,
+                        b->max_len);
+        if ((int64_t)b->num_seqs * c->seq_stride > c->num_rows)
+            return fail(DSA_ERR_INVALID_ARG, "%s: num_seqs * seq_stride exceeds num_rows", name);
+    }
+    return DSA_OK;
+}
+
+dsa::CacheView view(const dsa_cache* c) {
+    dsa::CacheView v;
+    v.data = c->data;
+    v.scale = c->scale;
+    v.num_rows = c->num_rows;
+    v.seq_stride = c->seq_stride;
+    v.page_table = c->page_table;
+    v.pt_stride = c->page_table_stride;
+    v.page_size = c->page_size > 0 ? c->page_size : 1;
+    return v;
+}
+
+dsa::BatchView view(const dsa_batch* b) {
+    dsa::BatchView v;
+    v.T = b->num_queries;
+    v.B = b->num_seqs;
+    v.cu_q = b->cu_q;
+    v.q_seq = b->q_seq;
+    v.q_len = b->q_len;
+    v.max_len = b->max_len;
+    v.max_q = b->max_q;
+    return v;
+}
+
+dsa_status check_indexer(const void* q, int32_t q_dtype, const float* weights, int32_t n_heads, int32_t head_dim,
+                         const dsa_cache* k_cache, const dsa_batch* batch) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (batch->num_queries > 0 && (!q || !weights)) return fail(DSA_ERR_INVALID_ARG, "indexer: q or weights is NULL");
+    if (head_dim != dsa::kIdxDim) return fail(DSA_ERR_UNSUPPORTED, "indexer: head_dim %d (only 128)", head_dim);
+    if (n_heads < 1 || n_heads > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "indexer: n_heads %d not in [1,128]", n_heads);
+    if (q_dtype != DSA_F32 && q_dtype != DSA_BF16 && q_dtype != DSA_FP8_E4M3)
+        return fail(DSA_ERR_INVALID_ARG, "indexer: unknown q dtype %d", q_dtype);
+    s = check_cache(k_cache, batch, dsa::kIdxDim, "k_cache");
+    if (s != DSA_OK) return s;
+    if (k_cache->dtype != q_dtype) return fail(DSA_ERR_UNSUPPORTED, "indexer: q and k_cache dtypes differ");
+    return DSA_OK;
+}
+
+dsa_status check_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
+                     const dsa_batch* batch, int32_t k, void* out) {
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (batch->num_queries > 0 && (!q || !out)) return fail(DSA_ERR_INVALID_ARG, "sparse_mla: q or out is NULL");
+    if (d_qk != dsa::kDqk || d_v != dsa::kDv)
+        return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: d_qk/d_v %d/%d (only 576/512)", d_qk, d_v);
+    if (n_heads < 1 || n_heads > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: n_heads %d not in [1,128]", n_heads);
+    if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
+    s = check_cache(latent, batch, dsa::kDqk, "latent");
+    if (s != DSA_OK) return s;
+    if (latent->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: latent cache must be bf16");
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+    switch (s) {
+        case DSA_OK: return "ok";
+        case DSA_ERR_INVALID_ARG: return "invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "unsupported";
+        case DSA_ERR_WORKSPACE: return "workspace too small";
+        case DSA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+const char* dsa_version(void) { return "libdsa 0.1 (gfx950)"; }
+
+size_t dsa_workspace_size(int32_t op, const dsa_batch* batch, int32_t k, int32_t n_heads, int32_t d_v) {
+    (void)d_v;
+    if (!batch || batch->num_queries <= 0) return 0;
+    const int T = batch->num_queries;
+    switch (op) {
+        case DSA_OP_INDEXER:
+        case DSA_OP_TOPK:
+            return 0;
+        case DSA_OP_SPARSE_MLA:
+            return k > 0 ? dsa::mla_workspace_bytes(T, k, n_heads) : 0;
+        case DSA_OP_FORWARD: {
+            if (k <= 0) return 0;
+            size_t bytes = 0;
+            if (batch->max_len > k) bytes += align256((size_t)T * score_ld(batch) * sizeof(float));
+            bytes += align256((size_t)T * k * sizeof(int32_t));
+            bytes += dsa::mla_workspace_bytes(T, k, n_heads);
+            return bytes;
+        }
+    }
+    return 0;
+}
+
+dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
+                              int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache, const dsa_batch* batch,
+                              float scale, float* scores, int64_t ld, hipStream_t stream) {
+    dsa_status s = check_indexer(q, q_dtype, weights, n_heads, head_dim, k_cache, batch);
+    if (s != DSA_OK) return s;
+    if (batch->num_queries > 0 && !scores) return fail(DSA_ERR_INVALID_ARG, "indexer: scores is NULL");
+    if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "indexer: ld %lld < max_len %d", (long long)ld, batch->max_len);
+    return hip_status(dsa::launch_indexer(q, q_dtype, q_scale, weights, n_heads, view(k_cache), view(batch), scale,
+                                          scores, ld, 0, stream),
+                      "indexer launch");
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
+    if (batch->num_queries > 0 && (!indices || (!scores && batch->max_len > k)))
+        return fail(DSA_ERR_INVALID_ARG, "topk: scores or indices is NULL");
+    if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "topk: ld %lld < max_len %d", (long long)ld, batch->max_len);
+    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, indices, stream), "topk launch");
+}
+
+dsa_status dsa_sparse_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
+                          const dsa_batch* batch, const int32_t* indices, int32_t k, float softmax_scale, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    dsa_status s = check_mla(q, n_heads, d_qk, d_v, latent, batch, k, out);
+    if (s != DSA_OK) return s;
+    if (batch->num_queries > 0 && !indices) return fail(DSA_ERR_INVALID_ARG, "sparse_mla: indices is NULL");
+    const size_t need = dsa::mla_workspace_bytes(batch->num_queries, k, n_heads);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DSA_ERR_WORKSPACE, "sparse_mla: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), view(batch), indices, k,
+                                             softmax_scale, (uint16_t*)out, lse, workspace, stream),
+                      "sparse_mla launch");
+}
+
+dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale, const float* weights,
+                       int32_t idx_heads, const dsa_cache* k_cache, float idx_scale, int32_t k, const void* q,
+                       int32_t n_heads, const dsa_cache* latent, float softmax_scale, const dsa_batch* batch,
+                       int32_t* indices_out, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    dsa_status s = check_mla(q, n_heads, dsa::kDqk, dsa::kDv, latent, batch, k, out);
+    if (s != DSA_OK) return s;
+    const bool need_scores = batch->max_len > k;
+    if (need_scores) {
+        s = check_indexer(q_idx, q_idx_dtype, weights, idx_heads, dsa::kIdxDim, k_cache, batch);
+        if (s != DSA_OK) return s;
+    }
+    const int T = batch->num_queries;
+    if (T == 0) return DSA_OK;
+    const int64_t ld = score_ld(batch);
+    size_t need = 0;
+    const size_t score_bytes = need_scores ? align256((size_t)T * ld * sizeof(float)) : 0;
+    const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
+    const size_t mla_bytes = dsa::mla_workspace_bytes(T, k, n_heads);
+    need = score_bytes + idx_bytes + mla_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    uint8_t* ws = (uint8_t*)workspace;
+    float* scores = need_scores ? (float*)ws : nullptr;
+    int32_t* idx = indices_out ? indices_out : (int32_t*)(ws + score_bytes);
+    void* mla_ws = mla_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
+
+    const dsa::BatchView bv = view(batch);
+    if (need_scores) {
+        s = hip_status(dsa::launch_indexer(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, view(k_cache), bv,
+                                           idx_scale, scores, ld, k, stream),
+                       "forward: indexer launch");
+        if (s != DSA_OK) return s;
+    }
+    s = hip_status(dsa::launch_topk(scores, ld, bv, k, idx, stream), "forward: topk launch");
+    if (s != DSA_OK) return s;
+    return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
+                                             (uint16_t*)out, lse, mla_ws, stream),
+                      "forward: sparse_mla launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+// indexer.hip -- lightning-indexer kernels for gfx950.
+//
+// Score of query t against visible token s (page "一文讀懂DeepSeek-V3.2核心技術DSA", section
+// "DSA 的四步工作流程", indexer-scoring step; page "DeepSeek 稀疏注意力路线（V3 / V3.2 / V4）",
+// section "两阶段流程", item 1):
+//     S[t,s] = scale * k_scale[s] * sum_j w'[t,j] * max(0, q[t,j,:] . k[s,:]),   w' = w * q_scale.
+// Folding q_scale into w' and applying k_scale after the head sum is exact because both scales are
+// non-negative and max(0, a x) = a max(0, x) for a >= 0.
+//
+// Three kernels:
+//   * fp8 decode:  one wave streams 256 keys of a sequence straight from HBM into MFMA operands
+//                  (v_mfma_f32_32x32x64_f8f6f4); the 1-2 query tokens of the sequence share every
+//                  key fetch.  HBM-bound: 132 bytes per key (128 fp8 + 4 scale).
+//   * bf16 prefill: four query tokens per workgroup (one per wave, 64 heads = two 32-row MFMA
+//                  tiles); 64-key tiles are staged once in LDS and shared by the four waves
+//                  (v_mfma_f32_32x32x16_bf16).  MFMA-bound.
+//   * generic:     any dtype / head count, one thread per (query, key); used for fp32 inputs and
+//                  shapes the MFMA kernels do not cover.
+// The ReLU-weight-sum epilogue runs on the MFMA accumulators in registers: the 32x32 accumulator
+// layout gives every lane 16 head rows of one key column, so the head sum is 16 in-register FMAs
+// per tile plus one cross-half shuffle.
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// generic path
+
+constexpr int kGenBlock = 256;
+
+__global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
+    const void* __restrict__ q, int dtype, const float* __restrict__ q_scale, const float* __restrict__ w,
+    int H, CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    extern __shared__ float gsm[];
+    float* qs = gsm;                 // [H][128], q * q_scale
+    float* wsh = gsm + H * kIdxDim;  // [H]
+    const int t = blockIdx.x;
+    const int b = bv.q_seq[t];
+    if (b < 0 || b >= bv.B) return;
+    const int n = min(bv.q_len[t], bv.max_len);
+    if (n <= skip_le) return;
+    const int s0 = blockIdx.y * kGenBlock;
+    if (s0 >= n) return;
+    for (int i = threadIdx.x; i < H * kIdxDim; i += kGenBlock) {
+        const int j = i / kIdxDim;
+        const float sc = q_scale ? q_scale[(int64_t)t * H + j] : 1.0f;
+        qs[i] = load_elem(q, dtype, (int64_t)t * H * kIdxDim + i) * sc;
+    }
+    for (int j = threadIdx.x; j < H; j += kGenBlock) wsh[j] = w[(int64_t)t * H + j];
+    __syncthreads();
+    const int s = s0 + threadIdx.x;
+    if (s >= n) return;
+    const int64_t row = cache_row(kc, b, s);
+    float kv[kIdxDim];
+    float ks = 0.0f;
+    if (row >= 0) {
+        for (int i = 0; i < kIdxDim; i++) kv[i] = load_elem(kc.data, dtype, row * kIdxDim + i);
+        ks = kc.scale ? kc.scale[row] : 1.0f;
+    } else {
+        for (int i = 0; i < kIdxDim; i++) kv[i] = 0.0f;
+    }
+    float total = 0.0f;
+    for (int j = 0; j < H; j++) {
+        float dot = 0.0f;
+        for (int i = 0; i < kIdxDim; i++) dot = fmaf(qs[j * kIdxDim + i], kv[i], dot);
+        total = fmaf(wsh[j], fmaxf(dot, 0.0f), total);
+    }
+    scores[(int64_t)t * ld + s] = scale * ks * total;
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp8 decode path: v_mfma_f32_32x32x64_f8f6f4.
+//
+// Operand layout (lane l, half g = l/32, column c = l%32): lane l holds row/column c and the 32
+// k-values 32g..32g+31 of the MFMA.  Both operands use the same dim assignment, so the contraction
+// is over the right pairs whatever order the hardware sums in: in k-step ks, half g carries dims
+// 64g + 32ks + [0,32).  A lane therefore reads 64 contiguous bytes of one key row.
+// Accumulator: lane l, register i holds column c (the key) and row 8(i/4) + 4g + i%4 (the head).
+
+constexpr int kDecKeysPerWave = 256;
+constexpr int kDecWaves = 4;
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, f32x16 c) {
+    // format 0 = e4m3 for both operands; block scales 127 = 2^0.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int NHS>
+__global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    constexpr int H = 32 * NHS;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    int qb = bv.cu_q[b], qe = bv.cu_q[b + 1];
+    qb = max(0, min(qb, bv.T));
+    qe = max(qb, min(qe, bv.T));
+    const int64_t key0 = (int64_t)blockIdx.x * (kDecWaves * kDecKeysPerWave) + wave * kDecKeysPerWave;
+
+    for (int t0 = qb; t0 < qe; t0 += 2) {
+        const int nq = min(2, qe - t0);
+        int n[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            n[u] = u < nq ? min(bv.q_len[t0 + u], bv.max_len) : 0;
+            if (n[u] <= skip_le) n[u] = 0;
+        }
+        const int nmax = max(n[0], n[1]);
+        if (key0 >= nmax) continue;
+
+        i32x8 qf[2][NHS][2];
+        float wr[2][NHS][16];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int t = t0 + (u < nq ? u : 0);
+#pragma unroll
+            for (int hs = 0; hs < NHS; hs++) {
+                const uint8_t* src = q + ((int64_t)t * H + 32 * hs + c) * kIdxDim + 64 * g;
+                qf[u][hs][0] = *(const i32x8*)(src);
+                qf[u][hs][1] = *(const i32x8*)(src + 32);
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int r = 32 * hs + 8 * (i / 4) + 4 * g + (i % 4);
+                    const float sc = q_scale ? q_scale[(int64_t)t * H + r] : 1.0f;
+                    wr[u][hs][i] = w[(int64_t)t * H + r] * sc;
+                }
+            }
+        }
+
+        const int64_t kend = min<int64_t>(key0 + kDecKeysPerWave, nmax);
+        for (int64_t sb = key0; sb < kend; sb += 32) {
+            const int64_t s = sb + c;
+            const int64_t row = cache_row(kc, b, min<int64_t>(s, nmax - 1));
+            i32x8 kf0 = {0, 0, 0, 0, 0, 0, 0, 0}, kf1 = kf0;
+            float ks = 0.0f;
+            if (row >= 0) {
+                const uint8_t* src = (const uint8_t*)kc.data + row * kIdxDim + 64 * g;
+                kf0 = *(const i32x8*)(src);
+                kf1 = *(const i32x8*)(src + 32);
+                ks = kc.scale ? kc.scale[row] : 1.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                if (u < nq && sb < n[u]) {
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int hs = 0; hs < NHS; hs++) {
+                        f32x16 acc = {};
+                        acc = mfma_fp8(qf[u][hs][0], kf0, acc);
+                        acc = mfma_fp8(qf[u][hs][1], kf1, acc);
+#pragma unroll
+                        for (int i = 0; i < 16; i++) sum = fmaf(wr[u][hs][i], fmaxf(acc[i], 0.0f), sum);
+                    }
+                    sum += __shfl_xor(sum, 32, 64);
+                    if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = scale * ks * sum;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 prefill path: v_mfma_f32_32x32x16_bf16, keys staged in LDS.
+//
+// Operand layout: lane l (half g, column c) holds row/column c and k-values 8g..8g+7.  In k-step
+// ks (0..7) half g carries dims 64g + 8ks + [0,8), so a lane reads 128 contiguous bytes of a key row.
+
+constexpr int kPreWaves = 4;
+constexpr int kPreTile = 64;      // keys per LDS tile
+constexpr int kPreRowB = 272;     // LDS row stride: 256 data bytes + 16 pad (bank spread)
+
+__device__ __forceinline__ f32x16 mfma_bf16_32(const bf16x8& a, const bf16x8& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NHS>
+__global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    constexpr int H = 32 * NHS;
+    constexpr int kChunksPerThread = kPreTile * 16 / (kPreWaves * 64);   // 16-byte chunks
+    __shared__ __attribute__((aligned(16))) uint8_t tile_lds[2][kPreTile * kPreRowB];
+    __shared__ int nmax_sh;
+
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    int qb = bv.cu_q[b], qe = bv.cu_q[b + 1];
+    qb = max(0, min(qb, bv.T));
+    qe = max(qb, min(qe, bv.T));
+    const int tq0 = qb + kPreWaves * (gridDim.x - 1 - blockIdx.x);   // longest groups first
+    if (tq0 >= qe) return;
+    const int t = tq0 + wave;
+    const bool has_q = t < qe;
+    int n = has_q ? min(bv.q_len[t], bv.max_len) : 0;
+    if (n <= skip_le) n = 0;
+    if (threadIdx.x == 0) nmax_sh = 0;
+    __syncthreads();
+    if (lane == 0) atomicMax(&nmax_sh, n);
+    __syncthreads();
+    const int nmax = nmax_sh;
+    if (nmax == 0) return;
+
+    bf16x8 qf[NHS][8];
+    float wr[NHS][16];
+#pragma unroll
+    for (int hs = 0; hs < NHS; hs++) {
+        const uint16_t* src = q + ((int64_t)(has_q ? t : tq0) * H + 32 * hs + c) * kIdxDim + 64 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) qf[hs][ks] = *(const bf16x8*)(src + 8 * ks);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int r = 32 * hs + 8 * (i / 4) + 4 * g + (i % 4);
+            const int tt = has_q ? t : tq0;
+            const float sc = q_scale ? q_scale[(int64_t)tt * H + r] : 1.0f;
+            wr[hs][i] = w[(int64_t)tt * H + r] * sc;
+        }
+    }
+
+    const int ntiles = (nmax + kPreTile - 1) / kPreTile;
+    i32x4 stage[kChunksPerThread];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+        for (int r = 0; r < kChunksPerThread; r++) {
+            const int ci = threadIdx.x + kPreWaves * 64 * r;
+            const int rr = ci >> 4, cc = ci & 15;
+            const int64_t s = (int64_t)tile * kPreTile + rr;
+            const int64_t row = s < nmax ? cache_row(kc, b, s) : -1;
+            stage[r] = row >= 0 ? *(const i32x4*)((const uint8_t*)kc.data + row * (kIdxDim * 2) + cc * 16)
+                                : i32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < kChunksPerThread; r++) {
+            const int ci = threadIdx.x + kPreWaves * 64 * r;
+            const int rr = ci >> 4, cc = ci & 15;
+            *(i32x4*)(&tile_lds[buf][rr * kPreRowB + cc * 16]) = stage[r];
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile++) {
+        const int buf = tile & 1;
+        if (tile + 1 < ntiles) load_tile(tile + 1);
+#pragma unroll
+        for (int sub = 0; sub < kPreTile / 32; sub++) {
+            const int sb = tile * kPreTile + sub * 32;
+            if (sb < n) {
+                bf16x8 kf[8];
+                const uint8_t* rowp = &tile_lds[buf][(sub * 32 + c) * kPreRowB + g * 128];
+#pragma unroll
+                for (int ks = 0; ks < 8; ks++) kf[ks] = *(const bf16x8*)(rowp + 16 * ks);
+                float sum = 0.0f;
+#pragma unroll
+                for (int hs = 0; hs < NHS; hs++) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int ks = 0; ks < 8; ks++) acc = mfma_bf16_32(qf[hs][ks], kf[ks], acc);
+#pragma unroll
+                    for (int i = 0; i < 16; i++) sum = fmaf(wr[hs][i], fmaxf(acc[i], 0.0f), sum);
+                }
+                sum += __shfl_xor(sum, 32, 64);
+                const int s = sb + c;
+                if (g == 0 && s < n) {
+                    float ks = 1.0f;
+                    if (kc.scale) {
+                        const int64_t row = cache_row(kc, b, s);
+                        ks = row >= 0 ? kc.scale[row] : 0.0f;
+                    }
+                    scores[(int64_t)t * ld + s] = scale * ks * sum;
+                }
+            }
+        }
+        if (tile + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const float* w, int H,
+                          const CacheView& kc, const BatchView& bv, float scale, float* scores,
+                          int64_t ld, int skip_le, hipStream_t st) {
+    if (bv.T == 0 || bv.max_len == 0 || bv.max_len <= skip_le) return hipSuccess;
+    const int nhs = (H % 32 == 0) ? H / 32 : 0;
+    if (dtype == DSA_FP8_E4M3 && (nhs == 1 || nhs == 2) && bv.max_q <= 8) {
+        dim3 grid((bv.max_len + kDecWaves * kDecKeysPerWave - 1) / (kDecWaves * kDecKeysPerWave), bv.B);
+        if (nhs == 1)
+            indexer_fp8_decode_kernel<1><<<grid, kDecWaves * 64, 0, st>>>(
+                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        else
+            indexer_fp8_decode_kernel<2><<<grid, kDecWaves * 64, 0, st>>>(
+                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        return hipGetLastError();
+    }
+    if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2)) {
+        dim3 grid((bv.max_q + kPreWaves - 1) / kPreWaves, bv.B);
+        if (nhs == 1)
+            indexer_bf16_prefill_kernel<1><<<grid, kPreWaves * 64, 0, st>>>(
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        else
+            indexer_bf16_prefill_kernel<2><<<grid, kPreWaves * 64, 0, st>>>(
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        return hipGetLastError();
+    }
+    const size_t shm = (size_t)H * (kIdxDim + 1) * sizeof(float);
+    if (shm > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)indexer_generic_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid(bv.T, (bv.max_len + kGenBlock - 1) / kGenBlock);
+    indexer_generic_kernel<<<grid, kGenBlock, shm, st>>>(q, dtype, q_scale, w, H, kc, bv, scale, scores, ld,
+                                                         skip_le);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,138 @@
+"""CPU checks of the C ABI: libdsa.so loads, exports every function include/dsa.h declares, and
+rejects bad arguments on the host before launching anything (no GPU needed: no call below
+reaches a kernel launch, the device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_sum_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.lib_path()):
+        from sparse_attention_sum_amd import build
+        build.build()
+    return dsa.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"^(?:dsa_status|size_t|const char\*)\s+(dsa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dsa_version().startswith(b"libdsa")
+    assert lib.dsa_status_string(0) == b"ok"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _batch(T=4, B=1, max_len=100, max_q=4):
+    return dsa._Batch(T, B, FAKE, FAKE, FAKE, max_len, max_q)
+
+
+def _cache(dim=128, dtype=dsa.DSA_FP8_E4M3, rows=1000, stride=100, pt=None, pt_stride=0, page=64):
+    return dsa._Cache(FAKE, None, dtype, dim, rows, stride, pt, pt_stride, page)
+
+
+def _idx(lib, head_dim=128, batch=None, cache=None, ld=128, q=FAKE, heads=64, dtype=dsa.DSA_FP8_E4M3):
+    b = batch or _batch()
+    c = cache or _cache()
+    return lib.dsa_indexer_scores(q, dtype, None, FAKE, heads, head_dim, ctypes.byref(c), ctypes.byref(b), 1.0,
+                                  FAKE, ld, None)
+
+
+def test_indexer_validation(lib):
+    assert _idx(lib, head_dim=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert b"head_dim" in lib.dsa_last_error()
+    assert _idx(lib, heads=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert _idx(lib, heads=129) == dsa.DSA_ERR_UNSUPPORTED
+    assert _idx(lib, q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert _idx(lib, ld=99) == dsa.DSA_ERR_INVALID_ARG
+    assert _idx(lib, dtype=7) == dsa.DSA_ERR_INVALID_ARG
+    assert _idx(lib, dtype=dsa.DSA_BF16) == dsa.DSA_ERR_UNSUPPORTED            # q / cache dtypes differ
+    assert _idx(lib, cache=_cache(dim=576)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _idx(lib, cache=_cache(stride=50)) == dsa.DSA_ERR_INVALID_ARG         # seq_stride < max_len
+    assert _idx(lib, cache=_cache(rows=50)) == dsa.DSA_ERR_INVALID_ARG           # B * stride > rows
+    assert _idx(lib, cache=_cache(pt=FAKE, pt_stride=1)) == dsa.DSA_ERR_INVALID_ARG   # 100 tokens need 2 pages
+    assert _idx(lib, cache=_cache(pt=FAKE, pt_stride=2, page=0)) == dsa.DSA_ERR_INVALID_ARG
+    assert _idx(lib, batch=_batch(max_q=0)) == dsa.DSA_ERR_INVALID_ARG
+    assert _idx(lib, batch=_batch(B=0)) == dsa.DSA_ERR_INVALID_ARG
+    bad = dsa._Batch(4, 1, None, FAKE, FAKE, 100, 4)
+    assert _idx(lib, batch=bad) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(FAKE, 2, None, FAKE, 64, 128, None, ctypes.byref(_batch()), 1.0, FAKE, 128,
+                                  None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_topk_validation(lib):
+    b = _batch()
+    assert lib.dsa_topk(FAKE, 128, ctypes.byref(b), 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, 128, ctypes.byref(b), 70000, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, 99, ctypes.byref(b), 16, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, 128, ctypes.byref(b), 16, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, 128, None, 16, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def _mla(lib, heads=128, dqk=576, dv=512, cache=None, k=2048, ws=None, ws_bytes=0, batch=None):
+    c = cache or _cache(dim=576, dtype=dsa.DSA_BF16)
+    b = batch or _batch(T=4)
+    return lib.dsa_sparse_mla(FAKE, heads, dqk, dv, ctypes.byref(c), ctypes.byref(b), FAKE, k, 0.04, FAKE, None,
+                              ws, ws_bytes, None)
+
+
+def test_sparse_mla_validation(lib):
+    assert _mla(lib, dqk=512) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(lib, dv=256) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(lib, heads=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(lib, heads=256) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(lib, k=0) == dsa.DSA_ERR_INVALID_ARG
+    assert _mla(lib, cache=_cache(dim=576, dtype=dsa.DSA_FP8_E4M3)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(lib, cache=_cache(dim=128, dtype=dsa.DSA_BF16)) == dsa.DSA_ERR_UNSUPPORTED
+    # 4 queries x 2048 slots need split partials in the workspace
+    assert _mla(lib) == dsa.DSA_ERR_WORKSPACE
+    assert b"workspace" in lib.dsa_last_error()
+    assert _mla(lib, ws=FAKE, ws_bytes=16) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_forward_validation(lib):
+    b = _batch(T=4, max_len=100)
+    kc = _cache()
+    lc = _cache(dim=576, dtype=dsa.DSA_BF16)
+    # k >= max_len: no scores needed, so a bad indexer head_dim is not even looked at, but the
+    # workspace is still required for the selection and the split partials
+    st = lib.dsa_forward(FAKE, dsa.DSA_FP8_E4M3, None, FAKE, 64, ctypes.byref(kc), 1.0, 16, FAKE, 128,
+                         ctypes.byref(lc), 0.04, ctypes.byref(b), None, FAKE, None, None, 0, None)
+    assert st == dsa.DSA_ERR_WORKSPACE
+    st = lib.dsa_forward(FAKE, dsa.DSA_BF16, None, FAKE, 64, ctypes.byref(kc), 1.0, 16, FAKE, 128,
+                         ctypes.byref(lc), 0.04, ctypes.byref(b), None, FAKE, None, None, 0, None)
+    assert st == dsa.DSA_ERR_UNSUPPORTED                     # indexer q / cache dtype mismatch
+
+
+def test_workspace_sizes(lib):
+    # decode: 64 queries, k = 2048 -> 4 splits of 512 slots
+    b = _batch(T=64, B=64, max_len=8192, max_q=1)
+    mla = lib.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512)
+    assert mla >= 64 * 4 * 128 * 513 * 4
+    fwd = lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, ctypes.byref(b), 2048, 128, 512)
+    assert fwd >= mla + 64 * 8192 * 4 + 64 * 2048 * 4
+    # prefill with many queries: one split, no partials
+    b = _batch(T=16384, B=1, max_len=16384, max_q=16384)
+    assert lib.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512) == 0
+    assert lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512) == 0
+    assert lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, None, 2048, 128, 512) == 0

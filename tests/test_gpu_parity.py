@@ -1,0 +1,280 @@
+"""GPU parity of libdsa against the CPU oracle (needs an MI355X and the built libdsa.so).
+
+Per workload: indexer scores within rtol * A (A = the dot products' condition magnitude, computed by
+the oracle on absolute values; rtol 1e-3 for f32/bf16 inputs, 2e-2 for fp8), the top-k set bit-exact
+when the oracle runs on the GPU's own scores, sparse MLA on the GPU's own indices within max-abs
+2e-2 / mean-abs 5e-3 / relative RMS 1e-2, and dsa_forward equal to the chained calls bit for bit.
+Full-size workloads are checked on sampled query rows; small workloads on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import NTHREADS, check_mla, check_scores, log, oracle_mla, oracle_scores, sets
+from sparse_attention_sum_amd import dsa, synth
+from sparse_attention_sum_amd.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+_current = {}
+
+
+def device_problem(spec):
+    key = spec.name
+    if key not in _current:
+        _current.clear()
+        torch.cuda.empty_cache()
+        log(f"building {spec.name} (T={spec.T}, B={spec.B}, max ctx={max(spec.ctx)})")
+        p = synth.build(spec)
+        _current[key] = to_device(p)
+        torch.cuda.synchronize()
+        log("uploaded")
+    return _current[key]
+
+
+def rtol_for(spec):
+    return 2e-2 if spec.idx_dtype == synth.FP8 else 1e-3
+
+
+def run_chain(dp, k):
+    """indexer -> top-k -> sparse MLA through the three separate entry points."""
+    b = dp.batch
+    ld = dsa.score_ld(b)
+    scores = dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, b, scale=dp.spec.idx_scale, ld=ld)
+    idx = dsa.dsa_topk(scores, ld, b, k)
+    out, lse = dsa.dsa_sparse_mla(dp.q_mla, dp.latent, b, idx, dp.spec.softmax_scale)
+    torch.cuda.synchronize()
+    return scores, idx, out, lse
+
+
+def check_problem(dp, rows_idx, rows_topk, rows_mla, label):
+    p, s = dp.problem, dp.spec
+    k = s.topk
+    scores, idx, out, lse = run_chain(dp, k)
+    log(f"{label}: GPU chain done")
+    # 1. indexer scores on sampled rows (rows with n <= ld only matter up to n)
+    rows = np.asarray(rows_idx, dtype=np.int32)
+    g = scores[torch.from_numpy(rows).long().cuda()].cpu().numpy()
+    ref = oracle_scores(p, qsel=rows, ld=g.shape[1])
+    A = oracle_scores(p, qsel=rows, ld=g.shape[1], absolute=True)
+    worst = check_scores(g, ref, A, p.q_len[rows], rtol_for(s))
+    log(f"{label}: indexer ok on {len(rows)} rows, worst |err|/A = {worst:.3e}")
+    # 2. top-k: oracle on the GPU's own scores, bit-exact sets
+    rows = np.asarray(rows_topk, dtype=np.int32)
+    g = scores[torch.from_numpy(rows).long().cuda()].cpu().numpy().astype(np.float64)
+    for r, t in enumerate(rows):
+        g[r, p.q_len[t]:] = -np.inf
+    want = oracle.topk(g, p.q_len, k, rows=rows, nthreads=NTHREADS)
+    got = idx[torch.from_numpy(rows).long().cuda()].cpu().numpy()
+    assert sets(got) == sets(want), f"{label}: top-k sets differ"
+    for r in range(len(rows)):     # ascending positions, then -1 padding
+        v = got[r][got[r] >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(got[r][len(v):] == -1)
+    log(f"{label}: top-k bit-exact on {len(rows)} rows")
+    # 3. sparse MLA on the GPU's own indices
+    rows = np.asarray(rows_mla, dtype=np.int32)
+    gi = idx[torch.from_numpy(rows).long().cuda()].cpu().numpy()
+    o_ref, l_ref = oracle_mla(p, gi, qsel=rows)
+    o_gpu = out[torch.from_numpy(rows).long().cuda()].float().cpu().numpy()
+    l_gpu = lse[torch.from_numpy(rows).long().cuda()].cpu().numpy()
+    mx, mean, rel = check_mla(o_gpu, l_gpu, o_ref, l_ref, label)
+    log(f"{label}: sparse MLA ok on {len(rows)} rows: max-abs {mx:.2e} mean-abs {mean:.2e} rel-RMS {rel:.2e}")
+    # 4. dsa_forward equals the chain bit for bit
+    ind2 = torch.empty_like(idx)
+    lse2 = torch.empty_like(lse)
+    out2, _, _ = dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, k, dp.q_mla, dp.latent, dp.batch,
+                                 s.softmax_scale, idx_scale=s.idx_scale, indices_out=ind2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(ind2, idx), f"{label}: forward indices differ from the chain"
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)), f"{label}: forward output differs"
+    assert torch.equal(lse2, lse)
+    log(f"{label}: dsa_forward == chain (bitwise)")
+    return scores, idx, out
+
+
+def _sample(T, q_len, k, extra=(), n=8, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(int(x) for x in extra if 0 <= x < T)
+    long_rows = np.nonzero(q_len > k)[0]
+    if len(long_rows):
+        rows.update(int(x) for x in rng.choice(long_rows, size=min(n, len(long_rows)), replace=False))
+    rows.update(int(x) for x in rng.choice(T, size=min(2, T), replace=False))
+    return sorted(rows)
+
+
+def test_config1_tiny_prefill_all_rows():
+    dp = device_problem(synth.spec_for(1))
+    T = dp.spec.T
+    check_problem(dp, range(T), range(T), range(0, T, 7), "tiny prefill")
+
+
+def test_config1_peaked_softmax():
+    dp = device_problem(synth.peaked_spec())
+    T = dp.spec.T
+    check_problem(dp, range(0, T, 97), range(T), range(0, T, 5), "peaked")
+
+
+def test_config2_batched_decode():
+    dp = device_problem(synth.spec_for(2))
+    p = dp.problem
+    rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=(0, 63))
+    check_problem(dp, rows, range(p.spec.T), rows, "decode B64 8K")
+
+
+def test_config3_long_prefill_sampled():
+    dp = device_problem(synth.spec_for(3))
+    p = dp.problem
+    edge = (0, 1, 2046, 2047, 2048, 2049, 4095, 16383)
+    rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=edge, n=6, seed=3)
+    topk_rows = sorted(set(rows) | set(range(2040, 2060)) | set(range(16384 - 256, 16384)))
+    check_problem(dp, rows, topk_rows, rows, "prefill 16K")
+
+
+def test_config4_mtp_paged_decode():
+    dp = device_problem(synth.spec_for(4))
+    p = dp.problem
+    rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=(0, 1, 62, 63), n=4, seed=4)
+    check_problem(dp, rows, range(p.spec.T), rows, "MTP decode paged 64K")
+
+
+def test_config5_ragged_paged_decode():
+    dp = device_problem(synth.spec_for(5))
+    p = dp.problem
+    assert (p.q_len <= 2048).sum() >= 3
+    T = p.spec.T
+    check_problem(dp, range(T), range(T), range(T), "ragged decode")
+
+
+# ---------------------------------------------------------------------------------------------
+# small workloads that walk tile edges and every kernel path
+
+
+SMALL = [
+    # name, ctx, nq, idx_heads, idx dtype, k, mla heads, paged
+    ("prefill-bf16-300", [300], [300], 64, synth.BF16, 64, 16, False),
+    ("prefill-bf16-h32-paged", [333], [333], 32, synth.BF16, 100, 32, True),
+    ("prefill-fp8-generic", [150], [150], 64, synth.FP8, 40, 128, False),
+    ("decode-fp8-ragged", [1, 31, 32, 33, 64, 65, 100, 257, 1000, 2049, 4097], [1] * 11, 64, synth.FP8, 64, 128, True),
+    ("mtp-fp8-h32", [70, 129, 3000], [2, 2, 2], 32, synth.FP8, 64, 64, False),
+    ("decode-bf16-contig", [500, 1025], [1, 1], 64, synth.BF16, 128, 48, False),
+    ("decode-f32-generic", [600, 90], [3, 1], 8, synth.F32, 50, 8, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_workloads_all_rows(case):
+    name, ctx, nq, hi, dt, k, h, paged = case
+    spec = synth.Spec(name, ctx=ctx, nq=nq, idx_heads=hi, idx_dtype=dt, topk=k, mla_heads=h, paged=paged, seed=11)
+    dp = device_problem(spec)
+    T = spec.T
+    check_problem(dp, range(T), range(T), range(T), name)
+
+
+def test_paged_equals_contiguous_bitwise():
+    """The same tokens through a page table and through a contiguous cache give identical bits."""
+    spec = synth.Spec("pg", ctx=[700, 1500], nq=[1, 2], idx_dtype=synth.FP8, topk=256, paged=True, seed=5)
+    p = synth.build(spec)
+    dp = to_device(p)
+    # contiguous copy of the same logical rows
+    B, L = spec.B, max(spec.ctx)
+    rows_of = lambda b, s: p.page_table[b, s // 64] * 64 + s % 64
+    lat = np.zeros((B * L, 576), np.uint16)
+    kc = np.zeros((B * L, 128), np.uint8)
+    ks = np.zeros(B * L, np.float32)
+    for b in range(B):
+        r = np.array([rows_of(b, s) for s in range(spec.ctx[b])])
+        lat[b * L:b * L + len(r)] = p.latent[r]
+        kc[b * L:b * L + len(r)] = p.k_idx[r]
+        ks[b * L:b * L + len(r)] = p.k_idx_scale[r]
+    kcache = dsa.Cache(torch.from_numpy(kc).view(torch.float8_e4m3fn).cuda(), torch.from_numpy(ks).cuda(), seq_stride=L)
+    lcache = dsa.Cache(torch.from_numpy(lat).view(torch.bfloat16).cuda(), seq_stride=L)
+    o1, l1, _ = dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, 256, dp.q_mla, dp.latent, dp.batch,
+                                spec.softmax_scale, lse=torch.empty(spec.T, 128, device="cuda"))
+    l2buf = torch.empty(spec.T, 128, device="cuda")
+    o2, l2, _ = dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, kcache, 256, dp.q_mla, lcache, dp.batch,
+                                spec.softmax_scale, lse=l2buf)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_deterministic_repeat():
+    spec = synth.spec_for(5)
+    dp = device_problem(spec)
+    a = run_chain(dp, spec.topk)
+    b = run_chain(dp, spec.topk)
+    for x, y in zip(a, b):
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y)
+
+
+def test_topk_stress_rows():
+    """Ties, signed zeros, constant rows, monotone rows, rows longer than the LDS cache."""
+    rng = np.random.default_rng(9)
+    rows, lens = [], []
+    L = 40000
+    def add(v):
+        row = np.full(L, np.nan, np.float32)
+        row[:len(v)] = v
+        rows.append(row); lens.append(len(v))
+    add(np.zeros(5000, np.float32))                                        # all equal
+    add(np.where(rng.random(6000) < 0.5, 0.0, -0.0).astype(np.float32))    # +0 / -0 mix
+    add(np.arange(7000, dtype=np.float32))                                 # monotone
+    add(-np.arange(7000, dtype=np.float32))
+    add(rng.integers(0, 5, 9000).astype(np.float32))                       # heavy ties
+    add(rng.standard_normal(L).astype(np.float32))                         # longer than LDS cache
+    add(np.concatenate([np.full(3000, 1e30), np.full(3000, -1e30)]).astype(np.float32))
+    add(rng.standard_normal(100).astype(np.float32))                       # n <= k
+    v = rng.standard_normal(5000).astype(np.float32); v[::2] = -np.inf     # -inf entries
+    add(v)
+    add(np.concatenate([np.full(100, 3.0), np.full(4000, 2.0)]).astype(np.float32))  # threshold inside a tie run
+    S = np.stack(rows)
+    q_len = np.array(lens, np.int32)
+    T = len(lens)
+    for k in (1, 37, 2048, 4096):
+        batch = dsa.Batch(cu_q=torch.tensor([0, T], dtype=torch.int32, device="cuda"),
+                          q_seq=torch.zeros(T, dtype=torch.int32, device="cuda"),
+                          q_len=torch.from_numpy(q_len).cuda(), max_len=L, max_q=T)
+        idx = dsa.dsa_topk(torch.from_numpy(S).cuda(), L, batch, k)
+        torch.cuda.synchronize()
+        S64 = S.astype(np.float64)
+        for r in range(T):
+            S64[r, q_len[r]:] = -np.inf
+        want = oracle.topk(S64, q_len, k)
+        assert sets(idx.cpu().numpy()) == sets(want), f"k={k}"
+
+
+def test_sparse_mla_user_indices_and_edge_cases():
+    """Unsorted indices, -1 in the middle, out-of-range entries, no valid entry, k not a multiple
+    of the tile, several head counts."""
+    rng = np.random.default_rng(10)
+    for H in (8, 16, 48, 128):
+        spec = synth.Spec(f"mla-H{H}", ctx=[300, 80, 5000], nq=[1, 1, 1], idx_dtype=synth.FP8, topk=100,
+                          mla_heads=H, seed=H)
+        p = synth.build(spec)
+        dp = to_device(p)
+        k = 100
+        idx = np.full((3, k), -1, np.int32)
+        idx[0, :70] = rng.permutation(300)[:70]
+        idx[0, 10] = -1; idx[0, 20] = 300; idx[0, 30] = 10 ** 6          # skipped entries
+        idx[1, :] = -1                                                    # nothing selected
+        idx[2, :] = rng.choice(5000, size=k, replace=False)
+        it = torch.from_numpy(idx).cuda()
+        out, lse = dsa.dsa_sparse_mla(dp.q_mla, dp.latent, dp.batch, it, spec.softmax_scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle_mla(p, idx)
+        check_mla(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"H={H}")
+        assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+def test_empty_batch_is_a_no_op():
+    T = 0
+    z = torch.zeros(0, dtype=torch.int32, device="cuda")
+    batch = dsa.Batch(cu_q=torch.zeros(2, dtype=torch.int32, device="cuda"), q_seq=z, q_len=z, max_len=0, max_q=1)
+    lat = dsa.Cache(torch.zeros(64, 576, dtype=torch.bfloat16, device="cuda"), seq_stride=64)
+    out, lse = dsa.dsa_sparse_mla(torch.zeros(0, 8, 576, dtype=torch.bfloat16, device="cuda"), lat, batch,
+                                  torch.zeros(0, 16, dtype=torch.int32, device="cuda"), 1 / 24)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 512)
