@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""DSA hot-path benchmark on one MI355X: tokens/s of dsa_forward (lightning indexer -> top-k ->
+sparse MLA) on a seeded synthetic workload, with the roofline of the dominant stage and the CPU
+oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one dsa_forward over the whole batch.  Inputs are resident in HBM before timing starts.
+Each step is timed with HIP events on the stream the library launches on; the last-level cache
+(256 MB MALL) and the L2s are flushed between steps, outside the events, so that gathered rows
+and cache pages come from HBM as they would in a model with many layers.  Rank 0 prints one JSON
+line.  Only one GPU is supported: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+WORKLOADS = {
+    "tiny-prefill-L1024": lambda s: s.spec_for(1),
+    "decode-B64-ctx8192": lambda s: s.spec_for(2),
+    "prefill-L16384": lambda s: s.spec_for(3),
+    "mtp-decode-B32x2-ctx65536-paged": lambda s: s.spec_for(4),
+    "ragged-decode-B16-paged": lambda s: s.spec_for(5),
+    "decode-B64-ctx16384": lambda s: s.sweep_spec(16384),
+    "decode-B64-ctx32768": lambda s: s.sweep_spec(32768),
+    "decode-B64-ctx65536": lambda s: s.sweep_spec(65536),
+    "decode-B64-ctx131072": lambda s: s.sweep_spec(131072),
+}
+DEFAULT_WORKLOAD = "decode-B64-ctx8192"
+CPU_SAMPLE = {"tiny-prefill-L1024": 1024, "decode-B64-ctx8192": 64, "prefill-L16384": 48,
+              "mtp-decode-B32x2-ctx65536-paged": 24, "ragged-decode-B16-paged": 16}
+
+KERNEL_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "sparse_mla": "sparse_mla.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check before timing")
+    ap.add_argument("--stage", default="all", choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy"],
+                    help="profiling aid: run only this stage --steps times (no JSON line)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# algorithmic work per launch
+
+
+def algorithmic(p, stage):
+    """(bytes, flops) the method must move / compute for one launch of a stage."""
+    s = p.spec
+    n = p.q_len.astype(np.int64)
+    k = s.topk
+    HI, H = s.idx_heads, s.mla_heads
+    long_ = n > k
+    if stage == "indexer":
+        elt = {"f32": 4, "bf16": 2, "fp8": 1}[s.idx_dtype]
+        kscale = 4 if s.idx_dtype == "fp8" else 0
+        # key cache read once per sequence (up to the longest query that needs scores)
+        nmax_seq = np.zeros(s.B, np.int64)
+        np.maximum.at(nmax_seq, p.q_seq, np.where(long_, n, 0))
+        kbytes = int(nmax_seq.sum()) * (128 * elt + kscale)
+        qbytes = int(long_.sum()) * HI * (128 * elt + 4 + (4 if s.idx_dtype == "fp8" else 0))
+        sbytes = int(n[long_].sum()) * 4
+        flops = int(n[long_].sum()) * HI * 128 * 2
+        return kbytes + qbytes + sbytes, flops
+    if stage == "topk":
+        return int(n[long_].sum()) * 4 + s.T * k * 4, 0
+    if stage == "sparse_mla":
+        cnt = np.minimum(n, k)
+        gather = int(cnt.sum()) * (576 * 2 + 4)
+        qo = s.T * H * (576 * 2 + 512 * 2 + 4)
+        flops = int(cnt.sum()) * H * (576 + 512) * 2
+        return gather + qo, flops
+    raise ValueError(stage)
+
+
+def bound_of(p, stage):
+    if stage == "indexer" and p.spec.idx_dtype != "fp8" and p.spec.B == 1 and p.spec.T > 256:
+        return "mfma", "bf16"
+    if stage == "sparse_mla" and p.spec.B == 1 and p.spec.T > 256:
+        return "mfma", "bf16"
+    return "hbm", None
+
+
+def source_hash(stage):
+    path = os.path.join(ROOT, "sparse_attention_sum_amd", "csrc", KERNEL_SOURCE[stage])
+    h = hashlib.sha256()
+    for f in (path, os.path.join(ROOT, "sparse_attention_sum_amd", "csrc", "common.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(f"{stage}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(stage):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------------
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the DSA path here is a single-GPU kernel library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    from sparse_attention_sum_amd import dsa, synth
+    from sparse_attention_sum_amd.device import to_device
+
+    dsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = WORKLOADS[args.workload](synth)
+    t_gen = time.time()
+    p = synth.build(spec)
+    dp = to_device(p, dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+    T, H, k = spec.T, spec.mla_heads, spec.topk
+    b = dp.batch
+    ld = dsa.score_ld(b)
+    stream = torch.cuda.current_stream()
+
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ind = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_FORWARD, b, k, H)), dtype=torch.uint8, device=dev)
+    scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=dev)
+    mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, k, H)
+    mla_ws = torch.empty(max(1, mla_ws_n), dtype=torch.uint8, device=dev)
+
+    def forward():
+        dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, k, dp.q_mla, dp.latent, b, spec.softmax_scale,
+                        idx_scale=spec.idx_scale, indices_out=ind, out=out, lse=lse, workspace=ws, stream=stream)
+
+    def stage_fn(stage):
+        if stage == "indexer":
+            return lambda: dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, b, spec.idx_scale,
+                                                   scores=scores, ld=ld, stream=stream)
+        if stage == "topk":
+            return lambda: dsa.dsa_topk(scores, ld, b, k, indices=ind, stream=stream)
+        if stage == "sparse_mla":
+            return lambda: dsa.dsa_sparse_mla(dp.q_mla, dp.latent, b, ind, spec.softmax_scale, out=out, lse=lse,
+                                              workspace=mla_ws if mla_ws_n else None, stream=stream)
+        return forward
+
+    flush_buf = torch.empty(384 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        if not args.no_flush:
+            flush_buf.add_(1.0)        # 384 MiB read + write: evicts the 256 MB MALL and the L2s
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        return ms, wall
+
+    # profiling aid: one stage only
+    if args.stage != "all":
+        if args.stage == "copy":
+            src = torch.empty(2 ** 30 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(args.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"stage": "copy", "bytes_read_per_launch": 2 ** 30, "bytes_written_per_launch": 2 ** 30}))
+            return
+        forward()
+        torch.cuda.synchronize()
+        fn = stage_fn(args.stage)
+        for _ in range(args.warmup):
+            fn()
+        ms, _ = timed(fn, args.steps)
+        print(json.dumps({"stage": args.stage, "workload": args.workload, "mean_us": float(ms.mean() * 1e3)}))
+        return
+
+    # correctness gate: spot-check a few queries against the oracle before timing
+    forward()
+    torch.cuda.synchronize()
+    check = None
+    if not args.no_check:
+        rows = np.unique(np.linspace(0, T - 1, num=min(T, 4)).astype(np.int32))
+        gi = ind[torch.from_numpy(rows).long().to(dev)].cpu().numpy()
+        o_ref, l_ref = oracle.sparse_mla(p.q_mla, p.latent, p.q_seq, p.q_len, gi, seq_stride=p.seq_stride,
+                                         page_table=p.page_table, page_size=spec.page_size,
+                                         softmax_scale=spec.softmax_scale, qsel=rows, nthreads=8)
+        o_gpu = out[torch.from_numpy(rows).long().to(dev)].float().cpu().numpy()
+        err = float(np.abs(o_gpu - o_ref).max())
+        assert err <= 2e-2, f"oracle spot check failed: max-abs {err}"
+        check = {"rows": int(len(rows)), "mla_max_abs_err": err}
+
+    for _ in range(args.warmup):
+        forward()
+    ms, wall = timed(forward, args.steps)
+    ms_per_step = float(ms.mean())
+    value = T / (ms_per_step / 1e3)
+
+    # per-stage timing through the separate entry points (same kernels, same launch shapes)
+    stages = {}
+    for st in ("indexer", "topk", "sparse_mla"):
+        if st != "sparse_mla" and p.max_len <= k:
+            continue
+        fn = stage_fn(st)
+        fn()
+        sms, _ = timed(fn, max(5, min(args.steps, 30)))
+        nbytes, flops = algorithmic(p, st)
+        stages[st] = {"mean_us": round(float(sms.mean() * 1e3), 3), "alg_bytes": nbytes, "alg_flops": flops}
+    forward()   # leave the outputs of a full forward in place
+    dom = max(stages, key=lambda s_: stages[s_]["mean_us"])
+    d = stages[dom]
+    bound, prec = bound_of(p, dom)
+    traffic = recorded_traffic(dom, args.workload)
+    if bound == "hbm":
+        achieved = d["alg_bytes"] / (d["mean_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        achieved = d["alg_flops"] / (d["mean_us"] * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS[prec]
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic}
+    roofline["kernel"] = dom
+    for st, v in stages.items():
+        v["hbm_GBs"] = round(v["alg_bytes"] / (v["mean_us"] * 1e-6) / 1e9, 1)
+        if v["alg_flops"]:
+            v["TFLOPs"] = round(v["alg_flops"] / (v["mean_us"] * 1e-6) / 1e12, 1)
+
+    # CPU baseline: the oracle, untuned, on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        nsample = min(T, CPU_SAMPLE.get(args.workload, 16))
+        rows = np.unique(np.linspace(0, T - 1, num=nsample).astype(np.int32))
+        threads = min(16, len(os.sched_getaffinity(0)))
+        t0 = time.perf_counter()
+        oracle.forward(p.q_idx, spec.idx_dtype, p.q_idx_scale, p.w, p.k_idx, spec.idx_dtype, p.k_idx_scale,
+                       p.q_mla, p.latent, p.q_seq, p.q_len, k, seq_stride=p.seq_stride, page_table=p.page_table,
+                       page_size=spec.page_size, scale=spec.idx_scale, softmax_scale=spec.softmax_scale,
+                       qsel=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(rows)} of {T} query tokens of {args.workload} (evenly spaced), fp64 oracle forward, "
+                         f"{dt:.2f} s wall"}
+
+    line = {
+        "metric": "DSA tokens/s (indexer+top-k+sparse MLA)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "query_tokens": T, "sequences": spec.B,
+                   "max_context": int(p.max_len), "topk": k, "indexer_heads": spec.idx_heads,
+                   "indexer_dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[spec.idx_dtype],
+                   "mla_heads": H, "latent": "bf16 576/512", "paged": spec.paged,
+                   "cache_state": "hot" if args.no_flush else "flushed between steps"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_us": stages,
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
+        "spot_check": check,
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
