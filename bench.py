@@ -7,8 +7,8 @@ oracle timed beside it.
 
 A step is one dsa_forward over the whole batch.  Inputs are resident in HBM before timing starts.
 Each step is timed with HIP events on the stream the library launches on; the last-level cache
-(256 MB MALL) and the L2s are flushed between steps, outside the events, so that gathered rows
-and cache pages come from HBM as they would in a model with many layers.  Rank 0 prints one JSON
+(256 MB MALL) and the L2s are flushed between steps (a 512 MiB read, outside the events), so that
+gathered rows and cache pages come from HBM as they would in a model with many layers.  Rank 0 prints one JSON
 line.  Only one GPU is supported: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -174,11 +174,15 @@ def main():
                                               workspace=mla_ws if mla_ws_n else None, stream=stream)
         return forward
 
-    flush_buf = torch.empty(384 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush_buf = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
 
     def flush():
+        # Read 512 MiB (more than the 256 MB MALL plus the L2s) so the step starts with caches
+        # holding only clean, unrelated lines.  A write-based flush would leave dirty lines whose
+        # write-back then competes with the step's own reads.
         if not args.no_flush:
-            flush_buf.add_(1.0)        # 384 MiB read + write: evicts the 256 MB MALL and the L2s
+            torch.sum(flush_buf, dim=0, keepdim=True, out=flush_out)
 
     def timed(fn, reps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]

@@ -121,7 +121,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int
  *            valid entries must be distinct
  *   out      [T][n_heads][d_v] bf16: sum_j softmax_j(softmax_scale * q.c_j) * c_j[:d_v]
  *   lse      [T][n_heads] floats (natural-log log-sum-exp of the scaled logits) or NULL
- * A query with no valid index gets out = 0 and lse = -inf.  1 <= n_heads <= 128. */
+ * A query with no valid index gets out = 0 and lse = -inf.  1 <= n_heads <= 128; softmax_scale must be
+ * positive and finite. */
 dsa_status dsa_sparse_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
                           const dsa_batch* batch, const int32_t* indices, int32_t k, float softmax_scale,
                           void* out, float* lse, void* workspace, size_t workspace_bytes,

@@ -2,6 +2,7 @@
 //
 // Every entry point validates its arguments on the host and returns before launching anything when
 // they are wrong.  Kernels are enqueued on the caller's stream; nothing here waits for the device.
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <cstdarg>
@@ -108,7 +109,7 @@ dsa_status check_indexer(const void* q, int32_t q_dtype, const float* weights, i
 }
 
 dsa_status check_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
-                     const dsa_batch* batch, int32_t k, void* out) {
+                     const dsa_batch* batch, int32_t k, void* out, float softmax_scale) {
     dsa_status s = check_batch(batch);
     if (s != DSA_OK) return s;
     if (batch->num_queries > 0 && (!q || !out)) return fail(DSA_ERR_INVALID_ARG, "sparse_mla: q or out is NULL");
@@ -119,6 +120,8 @@ dsa_status check_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, 
     s = check_cache(latent, batch, dsa::kDqk, "latent");
     if (s != DSA_OK) return s;
     if (latent->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: latent cache must be bf16");
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY)
+        return fail(DSA_ERR_INVALID_ARG, "sparse_mla: softmax_scale must be positive and finite");
     return DSA_OK;
 }
 
@@ -191,7 +194,7 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int
 dsa_status dsa_sparse_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
                           const dsa_batch* batch, const int32_t* indices, int32_t k, float softmax_scale, void* out,
                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    dsa_status s = check_mla(q, n_heads, d_qk, d_v, latent, batch, k, out);
+    dsa_status s = check_mla(q, n_heads, d_qk, d_v, latent, batch, k, out, softmax_scale);
     if (s != DSA_OK) return s;
     if (batch->num_queries > 0 && !indices) return fail(DSA_ERR_INVALID_ARG, "sparse_mla: indices is NULL");
     const size_t need = dsa::mla_workspace_bytes(batch->num_queries, k, n_heads);
@@ -207,7 +210,7 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        int32_t n_heads, const dsa_cache* latent, float softmax_scale, const dsa_batch* batch,
                        int32_t* indices_out, void* out, float* lse, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    dsa_status s = check_mla(q, n_heads, dsa::kDqk, dsa::kDv, latent, batch, k, out);
+    dsa_status s = check_mla(q, n_heads, dsa::kDqk, dsa::kDv, latent, batch, k, out, softmax_scale);
     if (s != DSA_OK) return s;
     const bool need_scores = batch->max_len > k;
     if (need_scores) {

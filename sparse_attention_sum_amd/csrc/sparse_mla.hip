@@ -6,21 +6,29 @@
 // up-projection comes afterwards):
 //     z_j = softmax_scale * q[t,h,:576] . c[I_j,:576],   out[t,h,:] = sum_j softmax(z)_j c[I_j,:512].
 //
-// Workgroup = (query, split of the index slots), 8 waves, 16 heads per wave (up to 128 heads).
-//   1. The split's valid indices are compacted (order kept) into an LDS list of storage rows.
-//   2. Tiles of 32 selected rows (32 x 1152 B) are gathered straight into LDS with gfx950's
-//      global_load_lds_dwordx4 (no staging registers), double-buffered: the next tile's loads are
-//      in flight while the current one is consumed.  One fetch of a row serves all heads -- the
-//      MQA form is what makes the sparse gather cheap.
-//   3. Logits S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys as rows, the wave's 16 heads as
-//      columns); the query block stays in registers for the whole split.
-//   4. Online softmax in base 2: each lane owns 8 keys of one head; the head's running max needs
-//      two cross-lane steps.
-//   5. O += P V with v_mfma_f32_16x16x32_bf16.  P is already in operand layout (no shuffle): its
-//      8 keys per lane define the k-slot order, and V is read in the matching order with the
-//      gfx950 LDS transpose load ds_read_b64_tr_b16.
-// A split writes normalised partial outputs and their log-sum-exp; a combine kernel merges splits
-// by log-sum-exp weights in a fixed order, so results are deterministic.
+// Workgroup = (query, split of the index slots), 8 waves = 4 head groups of 32 heads x 2 halves;
+// two waves per SIMD.  The two waves of a head group split the work so that each holds only half
+// of the query block and half of the output block (under 256 registers, which is what allows two
+// waves per SIMD):
+//   * logits: wave half h contracts query dims [288h, 288h + 288) against the tile, the partial
+//     logits are exchanged through LDS and both waves add them in the same order;
+//   * output: wave half h accumulates value dims [256h, 256h + 256).
+// Per tile:
+//   1. Tiles of 32 selected rows (32 x 1152 B) are gathered straight into LDS with gfx950's
+//      global_load_lds_dwordx4 (no staging registers), triple-buffered in three distinct LDS arrays
+//      so two tiles' loads overlap the current tile's math.  One fetch of a row serves all heads
+//      -- the MQA form is what makes the sparse gather cheap.
+//   2. Partial logits S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (32 keys as rows, the group's 32
+//      heads as columns).
+//   3. Softmax in base 2 against a fixed per-head reference (the head's max over the first tile):
+//      a lane holds 16 of the 32 keys of one head, the other 16 are in the lane 32 away.  The output
+//      block is never rescaled in the loop; a split whose logits climb more than 2^64 above the
+//      reference is redone in two passes (exact max, then accumulation).
+//   4. O += P V with v_mfma_f32_32x32x16_bf16.  P is already in operand layout (no shuffle): the 16
+//      keys a lane owns define the k-slot order of the two K=16 steps, and V is read in the matching
+//      order with the gfx950 LDS transpose load ds_read_b64_tr_b16.
+// A split writes its normalised partial output (bf16) and log-sum-exp; a combine kernel merges
+// splits by log-sum-exp weights in a fixed order, so results are deterministic.
 #include "kernels.h"
 
 namespace dsa {
@@ -28,40 +36,74 @@ namespace {
 
 constexpr int kMlaWaves = 8;
 constexpr int kMlaThreads = kMlaWaves * 64;
+constexpr int kHeadsPerGroup = 32;
+constexpr int kQkHalf = kDqk / 2;               // 288 query dims per wave half
+constexpr int kVHalf = kDv / 2;                 // 256 value dims per wave half
 constexpr int kTile = 32;                       // selected rows per LDS tile
 constexpr int kRowChunks = kDqk * 2 / 16;       // 72 16-byte chunks per latent row
 constexpr int kRowSlots = kRowChunks + 1;       // LDS row = 72 chunks + 1 pad chunk (bank spread)
 constexpr int kRowB = kRowSlots * 16;           // 1168 bytes
 constexpr int kTileSlots = kTile * kRowSlots;   // 2336 16-byte LDS slots per tile
 constexpr int kLoadsPerWave = (kTileSlots + kMlaThreads - 1) / kMlaThreads;
-constexpr int kMaxList = 4096;                  // index slots per split
+constexpr int kMaxList = 2048;                  // index slots per split
+constexpr int kAhead = 4;                       // logit operand reads in flight
+constexpr int kAheadV = 2;                      // value operand steps in flight
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kHeadroom = 64.0f;              // log2 margin above a head's reference max
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
+__device__ __forceinline__ bf16x8 tr_pair(const uint8_t* p0, const uint8_t* p1) {
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, int H, CacheView lat, BatchView bv, const int32_t* __restrict__ idx,
     int k, int per_split, int splits, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t msm[];
-    uint8_t* tiles = msm;                                         // [2][kTile][kRowB]
-    int32_t* rows = (int32_t*)(msm + 2 * kTile * kRowB);          // [per_split]
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+    // Three distinct LDS tiles: with fixed roles per (unrolled) iteration the compiler can tell that
+    // reads of one tile do not depend on the in-flight global->LDS loads into the others.
+    __shared__ __attribute__((aligned(16))) uint8_t tile_a[kTile * kRowB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_b[kTile * kRowB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_c[kTile * kRowB];
+    __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][4][64];   // partial-logit exchange
+    __shared__ int32_t rows[kMaxList];
     __shared__ int wcount[kMlaWaves];
 
-    const int t = blockIdx.x / splits, split = blockIdx.x % splits;
+    // XCD-aware order: consecutive workgroups go to different XCDs (round robin over 8), so the
+    // splits of one query take block ids 8 apart and share that XCD's L2 for the query block.
+    const int nb = gridDim.x;
+    const int bid = blockIdx.x;
+    const int lid = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+    const int t = lid / splits, split = lid % splits;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, j = lane & 15;
+    const int hg = wave >> 1, half = wave & 1;      // head group, half of the dims
+    const int c32 = lane & 31, g = lane >> 5;       // 32x32 operand layout: column / row c32, k-half g
     const int b = bv.q_seq[t];
     const bool seq_ok = b >= 0 && b < bv.B;
     const int n = seq_ok ? min(bv.q_len[t], bv.max_len) : 0;
     const int j0 = split * per_split, j1 = min(k, j0 + per_split);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-    // 1. compact the valid selected positions of this split into storage rows
+    // query half-block (loads issued first, so their latency overlaps the index compaction):
+    // lane (g, c32) holds head 32*hg + c32, dims 288*half + 16*kk + 8*g + [0, 8)
+    const int hq = kHeadsPerGroup * hg + c32;
+    const bool wave_on = kHeadsPerGroup * hg < H;
+    bf16x8 qf[kQkHalf / 16];
+    const bf16x8 zero8 = {};
+#pragma unroll
+    for (int kk = 0; kk < kQkHalf / 16; kk++)
+        qf[kk] = (wave_on && hq < H)
+                     ? *(const bf16x8*)(q + ((int64_t)t * H + hq) * kDqk + kQkHalf * half + 16 * kk + 8 * g)
+                     : zero8;
+
+    // 0. compact the valid selected positions of this split into storage rows
     int cnt = 0;
     for (int base = j0; base < j1; base += kMlaThreads) {
         const int slot = base + tid;
@@ -81,28 +123,14 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
         __syncthreads();
     }
 
-    // query block of this wave: lane (g, j) holds head 16*wave + j, dims 32*kk + 8*g + [0, 8)
-    const int hq = 16 * wave + j;
-    const bool wave_on = 16 * wave < H;
-    bf16x8 qf[kDqk / 32];
-    const bf16x8 zero8 = {};
-#pragma unroll
-    for (int kk = 0; kk < kDqk / 32; kk++)
-        qf[kk] = (wave_on && hq < H) ? *(const bf16x8*)(q + ((int64_t)t * H + hq) * kDqk + 32 * kk + 8 * g) : zero8;
-
-    f32x4 oacc[kDv / 16];
-#pragma unroll
-    for (int nd = 0; nd < kDv / 16; nd++) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
     const int ntiles = (cnt + kTile - 1) / kTile;
-    // 2. gather a tile straight into LDS (global_load_lds_dwordx4): wave instruction r of wave w
-    //    fills LDS slots [64 (8 r + w), +64); slot p holds chunk p % 73 of tile row p / 73 (the 73rd
-    //    slot of a row is padding and is not loaded).  Rows past the end of the list repeat the
-    //    last selected row, so every LDS value stays finite; their logits are masked to -inf.
+    // 1. gather a tile straight into LDS: wave instruction r of wave w fills LDS slots
+    //    [64 (8 r + w), +64); slot p holds chunk p % 73 of tile row p / 73 (the 73rd slot of a row
+    //    is padding and is not loaded).  Rows past the end of the list repeat the last selected
+    //    row, so every LDS value stays finite; their logits are masked to -inf.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto load_tile = [&](int tile, int buf) {
-        uint8_t* tb = tiles + buf * kTile * kRowB;
+    const int my_loads = (kTileSlots - wave_u * 64 + kMlaThreads - 1) / kMlaThreads;   // instructions per tile
+    auto load_tile = [&](int tile, uint8_t* tb) {
 #pragma unroll
         for (int r = 0; r < kLoadsPerWave; r++) {
             const int p0 = (r * kMlaWaves + wave_u) * 64;
@@ -118,146 +146,282 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
             }
         }
     };
-
-    if (ntiles > 0) load_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int tile = 0; tile < ntiles; tile++) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntiles) load_tile(tile + 1, buf ^ 1);
-        if (wave_on) {
-            const uint8_t* tb = tiles + buf * kTile * kRowB;
-            // 3. logits for keys 16*nt + 4*g + i (rows) x heads j (columns)
-            f32x4 sacc[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const uint8_t* rp = tb + (16 * nt + j) * kRowB + 16 * g;
-#pragma unroll
-                for (int kk = 0; kk < kDqk / 32; kk++) sacc[nt] = mfma16(*(const bf16x8*)(rp + 64 * kk), qf[kk], sacc[nt]);
-            }
-            // 4. online softmax; slot r of this lane is key 16*(r/4) + 4*g + r%4 of the tile
-            float z[8];
-#pragma unroll
-            for (int r = 0; r < 8; r++) {
-                const int key = tile * kTile + 16 * (r / 4) + 4 * g + (r % 4);
-                z[r] = key < cnt ? sacc[r / 4][r % 4] * scale_log2 : -INFINITY;
-            }
-            float mt = z[0];
-#pragma unroll
-            for (int r = 1; r < 8; r++) mt = fmaxf(mt, z[r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = fmaxf(m_run, mt);
-            const float mbase = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = exp2f(m_run - mbase);
-            float psum = 0.0f;
-            bf16x8 pf;
-#pragma unroll
-            for (int r = 0; r < 8; r++) {
-                const float p = exp2f(z[r] - mbase);
-                psum += p;
-                pf[r] = (__bf16)p;
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            float ao[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) ao[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-            for (int nd = 0; nd < kDv / 16; nd++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) oacc[nd][i] *= ao[i];
-            // 5. O[heads 4g+i][dims 16nd + j] += P V; V rows come transposed from LDS so that lane
-            //    (g, j) receives dim 16nd + j of keys 4g + [0,4) (first read) and 16 + 4g + [0,4).
-            const uint8_t* vp = tb + (4 * g + (j >> 2)) * kRowB + 8 * (j & 3);
-#pragma unroll
-            for (int nd = 0; nd < kDv / 16; nd++) {
-                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 32 * nd));
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * kRowB + 32 * nd));
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[nd] = mfma16(pf, vf, oacc[nd]);
-            }
+    // wait until the next tile to consume has landed; the newest tile's loads may stay in flight
+    auto wait_ahead = [&](bool next_exists, bool newest_in_flight) {
+        if (next_exists && newest_in_flight) {
+            if (my_loads == kLoadsPerWave)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave - 1) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    if (ntiles > 0) load_tile(0, tile_a);
+    if (ntiles > 1) load_tile(1, tile_b);
+
+    f32x16 oacc[kVHalf / 32];
+#pragma unroll
+    for (int nd = 0; nd < kVHalf / 32; nd++) oacc[nd] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    // V transpose-read address of this lane: 16-lane group G = lane/16 takes k-half g = G/2 and
+    // dims 16*(G%2) of each 32-dim block; lane jj of the group points at row 4g + jj/4 (+16m + 8h
+    // per step) and dims 4*(jj%4).
+    const int G = lane >> 4, jj = lane & 15;
+    const int v_off = (4 * g + (jj >> 2)) * kRowB + 32 * (G & 1) + 8 * (jj & 3) + 2 * kVHalf * half;
+
+    // 2. partial logits over this wave's half of the query dims; register i holds key
+    //    8*(i/4) + 4*g + i%4 of the tile for head c32
+    auto qk_tile = [&](const uint8_t* tb) -> f32x16 {
+        f32x16 sacc = {};
+        const uint8_t* rp = tb + c32 * kRowB + 16 * g + 2 * kQkHalf * half;
+        bf16x8 kb[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; u++) kb[u] = *(const bf16x8*)(rp + 32 * u);
+#pragma unroll
+        for (int kk = 0; kk < kQkHalf / 16; kk++) {
+            const bf16x8 a = kb[kk % kAhead];
+            if (kk + kAhead < kQkHalf / 16) kb[kk % kAhead] = *(const bf16x8*)(rp + 32 * (kk + kAhead));
+            sacc = mfma32(a, qf[kk], sacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int kk = 0; kk < kQkHalf / 16 - kAhead; kk++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        return sacc;
+    };
+    // the two halves' partial logits -> full (unscaled) logits; IEEE addition is commutative, so
+    // both waves of the pair get bit-identical sums.  Keys past the end of the list (last tile
+    // only) are masked to -inf.
+    auto logits = [&](int tile, const f32x16& part, float (&z)[16]) -> float {
+        f32x4* mine = &sx[wave][0][lane];
+#pragma unroll
+        for (int u = 0; u < 4; u++) mine[64 * u] = f32x4{part[4 * u], part[4 * u + 1], part[4 * u + 2], part[4 * u + 3]};
+        __syncthreads();
+        const f32x4* other = &sx[wave ^ 1][0][lane];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const f32x4 o = other[64 * u];
+#pragma unroll
+            for (int e = 0; e < 4; e++) z[4 * u + e] = part[4 * u + e] + o[e];
+        }
+        if ((tile + 1) * kTile > cnt) {
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                if (tile * kTile + 8 * (i / 4) + 4 * g + (i % 4) >= cnt) z[i] = -INFINITY;
+        }
+        float mt = z[0];
+#pragma unroll
+        for (int i = 1; i < 16; i++) mt = fmaxf(mt, z[i]);
+        return fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;   // scaled max over the 32 keys
+    };
+    // 4. O[heads 8(i/4) + 4g + i%4][dims 256*half + 32nd + c32] += P V.  Step m covers keys
+    //    16m + 8(r/4) + 4g + r%4 in k-slot r; the two transpose reads fetch rows 16m + 4g + [0,4)
+    //    and 16m + 8 + 4g + [0,4).
+    auto pv_tile = [&](f32x16 (&acc)[kVHalf / 32], const uint8_t* tb, const float (&z)[16], float mref) {
+        bf16x8 pf[2];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            // p = 2^(scale*log2e*z - mref); the raw v_exp_f32 is enough: its argument is at most
+            // kHeadroom and anything below 2^-126 may flush to zero
+            const float p = __builtin_amdgcn_exp2f(fmaf(z[i], scale_log2, -mref));
+            l_run += p;
+            pf[i / 8][i % 8] = (__bf16)p;
+        }
+        const uint8_t* vp = tb + v_off;
+        constexpr int kSteps = 2 * (kVHalf / 32);
+        bf16x8 vb[kAheadV];
+#pragma unroll
+        for (int u = 0; u < kAheadV; u++) {
+            const uint8_t* p0 = vp + (16 * (u % 2)) * kRowB + 64 * (u / 2);
+            vb[u] = tr_pair(p0, p0 + 8 * kRowB);
+        }
+#pragma unroll
+        for (int st = 0; st < kSteps; st++) {
+            const bf16x8 v = vb[st % kAheadV];
+            if (st + kAheadV < kSteps) {
+                const int nx = st + kAheadV;
+                const uint8_t* p0 = vp + (16 * (nx % 2)) * kRowB + 64 * (nx / 2);
+                vb[st % kAheadV] = tr_pair(p0, p0 + 8 * kRowB);
+            }
+            acc[st / 2] = mfma32(pf[st % 2], v, acc[st / 2]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAheadV, 0);
+#pragma unroll
+        for (int st = 0; st < kSteps - kAheadV; st++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAheadV, 0);
+    };
+
+    // 3. softmax reference: each head keeps the max of its first tile as a fixed reference, so the
+    //    output block is never rescaled inside the loop.  That is exact while no later logit
+    //    exceeds the reference by more than kHeadroom (log2 units): p <= 2^kHeadroom cannot
+    //    overflow and whatever underflows is below 2^-126 of the largest term.  Past that margin
+    //    the workgroup redoes the split in two passes with a fresh accumulator (exact max first).
+    //    Every wave takes part in the exchange barrier, also waves without heads.
+    bool over = false;
+    auto fast_tile = [&](int tile, const uint8_t* tb) {
+        const f32x16 part = wave_on ? qk_tile(tb) : f32x16{};
+        float z[16];
+        const float mt = logits(tile, part, z);
+        if (!wave_on) return;
+        if (tile == 0) m_run = mt;
+        over |= mt > m_run + kHeadroom;
+        pv_tile(oacc, tb, z, m_run);
+    };
+
+    wait_ahead(true, ntiles > 1);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 3) {
+        // tile i is consumed while tiles i+1 (issued earlier) and i+2 (issued now) are in flight
+        if (tile + 2 < ntiles) load_tile(tile + 2, tile_c);
+        fast_tile(tile, tile_a);
+        wait_ahead(tile + 1 < ntiles, tile + 2 < ntiles);
+        __syncthreads();
+        if (tile + 1 >= ntiles) break;
+        if (tile + 3 < ntiles) load_tile(tile + 3, tile_a);
+        fast_tile(tile + 1, tile_b);
+        wait_ahead(tile + 2 < ntiles, tile + 3 < ntiles);
+        __syncthreads();
+        if (tile + 2 >= ntiles) break;
+        if (tile + 4 < ntiles) load_tile(tile + 4, tile_b);
+        fast_tile(tile + 2, tile_c);
+        wait_ahead(tile + 3 < ntiles, tile + 4 < ntiles);
         __syncthreads();
     }
 
-    if (!wave_on) return;
-    float l = l_run + __shfl_xor(l_run, 16, 64);
-    l += __shfl_xor(l, 32, 64);                              // softmax denominator of head hq
-    const float lse_h = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-    float inv[4];
+    // 5. normalise and store (bf16 output when the split is the whole selection, else bf16 partials)
+    const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;   // padded heads
+    auto finish = [&](const f32x16 (&acc)[kVHalf / 32], float lsum, float mref) {
+        if (!wave_on) return;
+        const float l = lsum + __shfl_xor(lsum, 32, 64);        // softmax denominator of head hq
+        const float lse_h = l > 0.0f ? (mref + log2f(l)) * kLn2 : -INFINITY;
+        float inv[16];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float li = __shfl(l, 4 * g + i, 64);
-        inv[i] = li > 0.0f ? 1.0f / li : 0.0f;
-    }
-    if (splits == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int head = 16 * wave + 4 * g + i;
-            if (head < H) {
-                uint16_t* op = out + ((int64_t)t * H + head) * kDv + j;
-#pragma unroll
-                for (int nd = 0; nd < kDv / 16; nd++) op[16 * nd] = f32_to_bf16_bits(oacc[nd][i] * inv[i]);
-            }
+        for (int i = 0; i < 16; i++) {
+            const float li = __shfl(l, 8 * (i / 4) + 4 * g + (i % 4), 64);
+            inv[i] = li > 0.0f ? 1.0f / li : 0.0f;
         }
-        if (lse && g == 0 && hq < H) lse[(int64_t)t * H + hq] = lse_h;
-    } else {
-        float* po = part_o + ((int64_t)t * splits + split) * H * kDv;
+        if (splits == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int head = 16 * wave + 4 * g + i;
-            if (head < H) {
+            for (int i = 0; i < 16; i++) {
+                const int head = kHeadsPerGroup * hg + 8 * (i / 4) + 4 * g + (i % 4);
+                if (head < H) {
+                    uint16_t* op = out + ((int64_t)t * H + head) * kDv + kVHalf * half + c32;
 #pragma unroll
-                for (int nd = 0; nd < kDv / 16; nd++) po[(int64_t)head * kDv + 16 * nd + j] = oacc[nd][i] * inv[i];
+                    for (int nd = 0; nd < kVHalf / 32; nd++) op[32 * nd] = f32_to_bf16_bits(acc[nd][i] * inv[i]);
+                }
             }
+            if (lse && half == 0 && g == 0 && hq < H) lse[(int64_t)t * H + hq] = lse_h;
+        } else {
+            // bf16 partials in the accumulator's own lane order, 8 bytes per lane per store:
+            // [t][split][wave][nd][i/4][lane][i%4]; element (wave, nd, i, lane) is head
+            // 32*(wave/2) + 8*(i/4) + 4*(lane/32) + i%4, dim 256*(wave%2) + 32*nd + lane%32.
+            i32x2* po = (i32x2*)(part_o + ((int64_t)t * splits + split) * hp * kDv + (int64_t)wave * kHeadsPerGroup * kVHalf);
+#pragma unroll
+            for (int nd = 0; nd < kVHalf / 32; nd++)
+#pragma unroll
+                for (int ig = 0; ig < 4; ig++) {
+                    const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[nd][4 * ig] * inv[4 * ig]) |
+                                        ((uint32_t)f32_to_bf16_bits(acc[nd][4 * ig + 1] * inv[4 * ig + 1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[nd][4 * ig + 2] * inv[4 * ig + 2]) |
+                                        ((uint32_t)f32_to_bf16_bits(acc[nd][4 * ig + 3] * inv[4 * ig + 3]) << 16);
+                    po[(nd * 4 + ig) * 64 + lane] = i32x2{(int)lo, (int)hi};
+                }
+            if (half == 0 && g == 0) part_lse[((int64_t)t * splits + split) * hp + hq] = lse_h;
         }
-        if (g == 0 && hq < H) part_lse[((int64_t)t * splits + split) * H + hq] = lse_h;
+    };
+
+    if (!__syncthreads_or(over)) {
+        finish(oacc, l_run, m_run);
+        return;
     }
+    // rare: logits spread too far for a fixed reference -- exact max, then accumulate afresh
+    float m_exact = -INFINITY;
+    for (int tile = 0; tile < ntiles; tile++) {
+        __syncthreads();
+        load_tile(tile, tile_a);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const f32x16 part = wave_on ? qk_tile(tile_a) : f32x16{};
+        float z[16];
+        m_exact = fmaxf(m_exact, logits(tile, part, z));
+    }
+    f32x16 acc2[kVHalf / 32];
+#pragma unroll
+    for (int nd = 0; nd < kVHalf / 32; nd++) acc2[nd] = f32x16{};
+    l_run = 0.0f;
+    for (int tile = 0; tile < ntiles; tile++) {
+        __syncthreads();
+        load_tile(tile, tile_a);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const f32x16 part = wave_on ? qk_tile(tile_a) : f32x16{};
+        float z[16];
+        logits(tile, part, z);
+        if (wave_on) pv_tile(acc2, tile_a, z, m_exact);
+    }
+    finish(acc2, l_run, m_exact);
 }
 
-// Merge the splits of each (query, head): weights exp(lse_s - max), fixed order over s.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+// Merge the splits of each (query, head) with weights exp(lse_s - max), in a fixed order over s.
+// One thread per 4 heads x 1 dim of the partial layout written above.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_lse, int splits, int H,
                                                           int T, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= T * H) return;
-    const int lane = threadIdx.x & 63;
-    const int t = wid / H, h = wid % H;
-    float m = -INFINITY;
-    for (int s = 0; s < splits; s++) m = fmaxf(m, part_lse[((int64_t)t * splits + s) * H + h]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.0f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < splits; s++) {
-            const float wgt = expf(part_lse[((int64_t)t * splits + s) * H + h] - m);
-            wsum += wgt;
-            const f32x4* po = (const f32x4*)(part_o + (((int64_t)t * splits + s) * H + h) * kDv + lane * 8);
-            const f32x4 a = po[0], c = po[1];
+    const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;   // padded heads
+    const int per_q = hp * kDv / 4;                      // threads per query
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)T * per_q) return;
+    const int t = (int)(gid / per_q);
+    const int r = (int)(gid % per_q);
+    const int lane = r & 63, ig = (r >> 6) & 3, nd = (r >> 8) & 7, wave = r >> 11;
+    const int head0 = kHeadsPerGroup * (wave >> 1) + 8 * ig + 4 * (lane >> 5);
+    if (head0 >= H) return;
+    const int dim = kVHalf * (wave & 1) + 32 * nd + (lane & 31);
+    float m[4], wsum[4], acc[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                acc[e] = fmaf(wgt, a[e], acc[e]);
-                acc[4 + e] = fmaf(wgt, c[e], acc[4 + e]);
-            }
+    for (int e = 0; e < 4; e++) {
+        m[e] = -INFINITY;
+        wsum[e] = 0.0f;
+        acc[e] = 0.0f;
+    }
+    for (int s = 0; s < splits; s++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) m[e] = fmaxf(m[e], part_lse[((int64_t)t * splits + s) * hp + head0 + e]);
+    for (int s = 0; s < splits; s++) {
+        const i32x2 raw = ((const i32x2*)part_o)[((int64_t)t * splits + s) * per_q + r];
+        const float v[4] = {bf16_bits_to_f32((uint16_t)(raw[0] & 0xffff)), bf16_bits_to_f32((uint16_t)((uint32_t)raw[0] >> 16)),
+                            bf16_bits_to_f32((uint16_t)(raw[1] & 0xffff)), bf16_bits_to_f32((uint16_t)((uint32_t)raw[1] >> 16))};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float ls = part_lse[((int64_t)t * splits + s) * hp + head0 + e];
+            const float wgt = m[e] == -INFINITY ? 0.0f : expf(ls - m[e]);
+            wsum[e] += wgt;
+            acc[e] = fmaf(wgt, v[e], acc[e]);
         }
     }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    uint16_t* op = out + ((int64_t)t * H + h) * kDv + lane * 8;
-    uint32_t packed[4];
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-        packed[e] = (uint32_t)f32_to_bf16_bits(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * e + 1] * inv) << 16);
-    *(i32x4*)op = i32x4{(int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]};
-    if (lse && lane == 0) lse[(int64_t)t * H + h] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
+    for (int e = 0; e < 4; e++) {
+        if (head0 + e >= H) break;
+        const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
+        out[((int64_t)t * H + head0 + e) * kDv + dim] = f32_to_bf16_bits(acc[e] * inv);
+        if (lse && nd == 0 && (wave & 1) == 0 && (lane & 31) == 0)
+            lse[(int64_t)t * H + head0 + e] = wsum[e] > 0.0f ? m[e] + logf(wsum[e]) : -INFINITY;
+    }
 }
 
 }  // namespace
 
 int mla_splits(int T, int k) {
     if (T <= 0 || k <= 0) return 1;
-    int s = (256 + T - 1) / T;                 // aim at one 8-wave workgroup per CU
+    int s = (256 + T - 1) / T;                 // aim at one workgroup per CU
     s = min(s, max(1, k / 64));                // at least 64 index slots per split
     s = max(s, (k + kMaxList - 1) / kMaxList); // the LDS index list holds kMaxList slots
     return max(1, s);
@@ -266,8 +430,9 @@ int mla_splits(int T, int k) {
 size_t mla_workspace_bytes(int T, int k, int H) {
     const int s = mla_splits(T, k);
     if (s == 1) return 0;
-    const size_t po = (size_t)T * s * H * kDv * sizeof(float);
-    const size_t pl = (size_t)T * s * H * sizeof(float);
+    const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;
+    const size_t po = (size_t)T * s * hp * kDv * sizeof(uint16_t);
+    const size_t pl = (size_t)T * s * hp * sizeof(float);
     return ((po + 255) & ~(size_t)255) + pl;
 }
 
@@ -277,23 +442,22 @@ hipError_t launch_sparse_mla(const uint16_t* q, int H, const CacheView& lat, con
     if (bv.T == 0) return hipSuccess;
     const int splits = mla_splits(bv.T, k);
     const int per_split = (k + splits - 1) / splits;
-    const size_t shm = (size_t)2 * kTile * kRowB + (size_t)per_split * sizeof(int32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)shm);
-    if (e != hipSuccess) return e;
-    float* part_o = nullptr;
+    uint16_t* part_o = nullptr;
     float* part_lse = nullptr;
     if (splits > 1) {
-        part_o = (float*)ws;
-        const size_t po = (size_t)bv.T * splits * H * kDv * sizeof(float);
+        part_o = (uint16_t*)ws;
+        const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;
+        const size_t po = (size_t)bv.T * splits * hp * kDv * sizeof(uint16_t);
         part_lse = (float*)((uint8_t*)ws + ((po + 255) & ~(size_t)255));
     }
     const float scale_log2 = softmax_scale * 1.44269504088896340736f;
-    sparse_mla_kernel<<<bv.T * splits, kMlaThreads, shm, st>>>(q, H, lat, bv, idx, k, per_split, splits, scale_log2,
+    hipError_t e;
+    sparse_mla_kernel<<<bv.T * splits, kMlaThreads, 0, st>>>(q, H, lat, bv, idx, k, per_split, splits, scale_log2,
                                                               out, lse, part_o, part_lse);
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    const int blocks = (bv.T * H + 3) / 4;
+    const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;
+    const int blocks = (int)(((int64_t)bv.T * hp * kDv / 4 + 255) / 256);
     mla_combine_kernel<<<blocks, 256, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse);
     return hipGetLastError();
 }
