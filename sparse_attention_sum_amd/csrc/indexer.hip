@@ -9,8 +9,8 @@
 //
 // Three kernels:
 //   * fp8 decode:  one wave streams 256 keys of a sequence straight from HBM into MFMA operands
-//                  (v_mfma_f32_32x32x64_f8f6f4); the 1-2 query tokens of the sequence share every
-//                  key fetch.  HBM-bound: 132 bytes per key (128 fp8 + 4 scale).
+//                  (v_mfma_f32_32x32x64_f8f6f4), several 32-key subtiles in flight; the 1-2 query
+//                  tokens of a pass share every key fetch.  HBM-bound: 132 bytes per key (128 fp8 + 4 scale).
 //   * bf16 prefill: four query tokens per workgroup (one per wave, 64 heads = two 32-row MFMA
 //                  tiles); 64-key tiles are staged once in LDS and shared by the four waves
 //                  (v_mfma_f32_32x32x16_bf16).  MFMA-bound.
@@ -86,11 +86,18 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, f32x1
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int NHS>
+// QG query tokens of one sequence share each key fetch (1 for plain decode, 2 for two-token
+// speculative decode).  A wave keeps PF key subtiles (32 keys each) in flight: the loads of subtile
+// i + PF are issued as soon as subtile i has been consumed, so the wave never waits for HBM latency
+// more than once per PF subtiles.  Loads past the end of the context are clamped to its last token
+// (in bounds; their scores are not stored), which keeps the loop free of branches around loads.
+template <int NHS, int QG>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
     constexpr int H = 32 * NHS;
+    constexpr int PF = QG == 1 ? 4 : 2;
+    constexpr int kSub = kDecKeysPerWave / 32;
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
@@ -99,21 +106,40 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
     qe = max(qb, min(qe, bv.T));
     const int64_t key0 = (int64_t)blockIdx.x * (kDecWaves * kDecKeysPerWave) + wave * kDecKeysPerWave;
 
-    for (int t0 = qb; t0 < qe; t0 += 2) {
-        const int nq = min(2, qe - t0);
-        int n[2];
+    for (int t0 = qb; t0 < qe; t0 += QG) {
+        const int nq = min(QG, qe - t0);
+        int n[QG];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
+        for (int u = 0; u < QG; u++) {
             n[u] = u < nq ? min(bv.q_len[t0 + u], bv.max_len) : 0;
             if (n[u] <= skip_le) n[u] = 0;
         }
-        const int nmax = max(n[0], n[1]);
+        int nmax = n[0];
+#pragma unroll
+        for (int u = 1; u < QG; u++) nmax = max(nmax, n[u]);
         if (key0 >= nmax) continue;
 
-        i32x8 qf[2][NHS][2];
-        float wr[2][NHS][16];
+        // key subtile ring: lane (g, c) holds dims 64g..64g+63 of key key0 + 32*sub + c
+        i32x8 kf[PF][2];
+        float ks[PF];
+        bool kv[PF];
+        auto load_keys = [&](int j, int sub) {
+            const int64_t s = min<int64_t>(key0 + 32 * sub + c, nmax - 1);
+            const int64_t row = cache_row(kc, b, s);
+            kv[j] = row >= 0;
+            const int64_t r = row >= 0 ? row : 0;
+            const uint8_t* src = (const uint8_t*)kc.data + r * kIdxDim + 64 * g;
+            kf[j][0] = *(const i32x8*)(src);
+            kf[j][1] = *(const i32x8*)(src + 32);
+            ks[j] = kc.scale ? kc.scale[r] : 1.0f;
+        };
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
+        for (int j = 0; j < PF; j++) load_keys(j, j);
+
+        i32x8 qf[QG][NHS][2];
+        float wr[QG][NHS][16];
+#pragma unroll
+        for (int u = 0; u < QG; u++) {
             const int t = t0 + (u < nq ? u : 0);
 #pragma unroll
             for (int hs = 0; hs < NHS; hs++) {
@@ -129,34 +155,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
             }
         }
 
-        const int64_t kend = min<int64_t>(key0 + kDecKeysPerWave, nmax);
-        for (int64_t sb = key0; sb < kend; sb += 32) {
+#pragma unroll
+        for (int sub = 0; sub < kSub; sub++) {
+            const int j = sub % PF;
+            const int64_t sb = key0 + 32 * sub;
             const int64_t s = sb + c;
-            const int64_t row = cache_row(kc, b, min<int64_t>(s, nmax - 1));
-            i32x8 kf0 = {0, 0, 0, 0, 0, 0, 0, 0}, kf1 = kf0;
-            float ks = 0.0f;
-            if (row >= 0) {
-                const uint8_t* src = (const uint8_t*)kc.data + row * kIdxDim + 64 * g;
-                kf0 = *(const i32x8*)(src);
-                kf1 = *(const i32x8*)(src + 32);
-                ks = kc.scale ? kc.scale[row] : 1.0f;
-            }
+            // an invalid page reads as an all-zero row
+            const i32x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+            const i32x8 k0 = kv[j] ? kf[j][0] : zero, k1 = kv[j] ? kf[j][1] : zero;
+            const float ksj = kv[j] ? ks[j] : 0.0f;
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
-                if (u < nq && sb < n[u]) {
-                    float sum = 0.0f;
+            for (int u = 0; u < QG; u++) {
+                float sum = 0.0f;
 #pragma unroll
-                    for (int hs = 0; hs < NHS; hs++) {
-                        f32x16 acc = {};
-                        acc = mfma_fp8(qf[u][hs][0], kf0, acc);
-                        acc = mfma_fp8(qf[u][hs][1], kf1, acc);
+                for (int hs = 0; hs < NHS; hs++) {
+                    f32x16 acc = {};
+                    acc = mfma_fp8(qf[u][hs][0], k0, acc);
+                    acc = mfma_fp8(qf[u][hs][1], k1, acc);
 #pragma unroll
-                        for (int i = 0; i < 16; i++) sum = fmaf(wr[u][hs][i], fmaxf(acc[i], 0.0f), sum);
-                    }
-                    sum += __shfl_xor(sum, 32, 64);
-                    if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = scale * ks * sum;
+                    for (int i = 0; i < 16; i++) sum = fmaf(wr[u][hs][i], fmaxf(acc[i], 0.0f), sum);
                 }
+                sum += __shfl_xor(sum, 32, 64);
+                if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = scale * ksj * sum;
             }
+            if (sub + PF < kSub) load_keys(j, sub + PF);
         }
     }
 }
@@ -290,12 +312,19 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
     const int nhs = (H % 32 == 0) ? H / 32 : 0;
     if (dtype == DSA_FP8_E4M3 && (nhs == 1 || nhs == 2) && bv.max_q <= 8) {
         dim3 grid((bv.max_len + kDecWaves * kDecKeysPerWave - 1) / (kDecWaves * kDecKeysPerWave), bv.B);
-        if (nhs == 1)
-            indexer_fp8_decode_kernel<1><<<grid, kDecWaves * 64, 0, st>>>(
-                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
-        else
-            indexer_fp8_decode_kernel<2><<<grid, kDecWaves * 64, 0, st>>>(
-                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        const uint8_t* q8 = (const uint8_t*)q;
+        const int block = kDecWaves * 64;
+        if (bv.max_q == 1) {
+            if (nhs == 1)
+                indexer_fp8_decode_kernel<1, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+            else
+                indexer_fp8_decode_kernel<2, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        } else {
+            if (nhs == 1)
+                indexer_fp8_decode_kernel<1, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+            else
+                indexer_fp8_decode_kernel<2, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        }
         return hipGetLastError();
     }
     if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2)) {

@@ -370,50 +370,60 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     finish(acc2, l_run, m_exact);
 }
 
-// Merge the splits of each (query, head) with weights exp(lse_s - max), in a fixed order over s.
-// One thread per 4 heads x 1 dim of the partial layout written above.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse, int splits, int H,
-                                                          int T, uint16_t* __restrict__ out, float* __restrict__ lse) {
+// Merge the splits of each (query, head) with weights exp(lse_s - lse), in a fixed order over s.
+// One workgroup per (query, wave slot) = 32 heads x 256 dims: the weights of the slot's heads are
+// computed once into LDS, then each thread folds 16-byte chunks of the splits' partials.
+constexpr int kCombThreads = 256;
+constexpr int kMaxSplitsComb = 64;
+
+__global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                                   const float* __restrict__ part_lse, int splits,
+                                                                   int H, int T, uint16_t* __restrict__ out,
+                                                                   float* __restrict__ lse) {
+    __shared__ float wts[kMaxSplitsComb][kHeadsPerGroup];
     const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;   // padded heads
-    const int per_q = hp * kDv / 4;                      // threads per query
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)T * per_q) return;
-    const int t = (int)(gid / per_q);
-    const int r = (int)(gid % per_q);
-    const int lane = r & 63, ig = (r >> 6) & 3, nd = (r >> 8) & 7, wave = r >> 11;
-    const int head0 = kHeadsPerGroup * (wave >> 1) + 8 * ig + 4 * (lane >> 5);
-    if (head0 >= H) return;
-    const int dim = kVHalf * (wave & 1) + 32 * nd + (lane & 31);
-    float m[4], wsum[4], acc[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        m[e] = -INFINITY;
-        wsum[e] = 0.0f;
-        acc[e] = 0.0f;
+    const int nslots = hp / kHeadsPerGroup * 2;
+    const int t = blockIdx.x / nslots, slot = blockIdx.x % nslots;
+    const int hg = slot >> 1, half = slot & 1;
+    const int tid = threadIdx.x;
+    if (tid < kHeadsPerGroup) {
+        const int head = kHeadsPerGroup * hg + tid;
+        const float* pl = part_lse + (int64_t)t * splits * hp + head;
+        float m = -INFINITY;
+        for (int s = 0; s < splits; s++) m = fmaxf(m, pl[(int64_t)s * hp]);
+        float wsum = 0.0f;
+        for (int s = 0; s < splits; s++) wsum += m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m);
+        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+        for (int s = 0; s < splits; s++) wts[s][tid] = m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m) * inv;
+        if (lse && half == 0 && head < H) lse[(int64_t)t * H + head] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
     }
-    for (int s = 0; s < splits; s++)
+    __syncthreads();
+    // chunk c (16 bytes = 8 bf16) of the slot: row rho = c/32 (nd = rho/4, ig = rho%4), partial lanes
+    // L = 2*(c%32) and L+1, each with 4 consecutive heads 8*ig + 4*(L/32) + e at dims 32*nd + L%32 (+1)
+    constexpr int kChunks = kHeadsPerGroup * kVHalf / 8;
+    for (int c = tid; c < kChunks; c += kCombThreads) {
+        const int rho = c >> 5, nd = rho >> 2, ig = rho & 3, L = 2 * (c & 31);
+        const int hl0 = 8 * ig + 4 * (L >> 5);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; s++) {
+            const i32x4 raw = *(const i32x4*)(part_o + ((int64_t)t * splits + s) * hp * kDv +
+                                              (int64_t)slot * kHeadsPerGroup * kVHalf + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 4; e++) m[e] = fmaxf(m[e], part_lse[((int64_t)t * splits + s) * hp + head0 + e]);
-    for (int s = 0; s < splits; s++) {
-        const i32x2 raw = ((const i32x2*)part_o)[((int64_t)t * splits + s) * per_q + r];
-        const float v[4] = {bf16_bits_to_f32((uint16_t)(raw[0] & 0xffff)), bf16_bits_to_f32((uint16_t)((uint32_t)raw[0] >> 16)),
-                            bf16_bits_to_f32((uint16_t)(raw[1] & 0xffff)), bf16_bits_to_f32((uint16_t)((uint32_t)raw[1] >> 16))};
+            for (int e = 0; e < 8; e++) {
+                const uint32_t wd = (uint32_t)raw[e / 2];
+                const float v = bf16_bits_to_f32((uint16_t)(e % 2 ? wd >> 16 : wd & 0xffff));
+                acc[e] = fmaf(wts[s][hl0 + (e % 4)], v, acc[e]);
+            }
+        }
+        const int dim = kVHalf * half + 32 * nd + (L & 31);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const float ls = part_lse[((int64_t)t * splits + s) * hp + head0 + e];
-            const float wgt = m[e] == -INFINITY ? 0.0f : expf(ls - m[e]);
-            wsum[e] += wgt;
-            acc[e] = fmaf(wgt, v[e], acc[e]);
+            const int head = kHeadsPerGroup * hg + hl0 + e;
+            if (head < H) {
+                const uint32_t pair = (uint32_t)f32_to_bf16_bits(acc[e]) | ((uint32_t)f32_to_bf16_bits(acc[4 + e]) << 16);
+                *(uint32_t*)(out + ((int64_t)t * H + head) * kDv + dim) = pair;
+            }
         }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        if (head0 + e >= H) break;
-        const float inv = wsum[e] > 0.0f ? 1.0f / wsum[e] : 0.0f;
-        out[((int64_t)t * H + head0 + e) * kDv + dim] = f32_to_bf16_bits(acc[e] * inv);
-        if (lse && nd == 0 && (wave & 1) == 0 && (lane & 31) == 0)
-            lse[(int64_t)t * H + head0 + e] = wsum[e] > 0.0f ? m[e] + logf(wsum[e]) : -INFINITY;
     }
 }
 
@@ -424,7 +434,7 @@ int mla_splits(int T, int k) {
     int s = (256 + T - 1) / T;                 // aim at one workgroup per CU
     s = min(s, max(1, k / 64));                // at least 64 index slots per split
     s = max(s, (k + kMaxList - 1) / kMaxList); // the LDS index list holds kMaxList slots
-    return max(1, s);
+    return max(1, min(s, kMaxSplitsComb));
 }
 
 size_t mla_workspace_bytes(int T, int k, int H) {
@@ -457,8 +467,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, int H, const CacheView& lat, con
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;
-    const int blocks = (int)(((int64_t)bv.T * hp * kDv / 4 + 255) / 256);
-    mla_combine_kernel<<<blocks, 256, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse);
+    const int blocks = bv.T * (hp / kHeadsPerGroup) * 2;
+    mla_combine_kernel<<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse);
     return hipGetLastError();
 }
 

@@ -20,17 +20,65 @@ constexpr int kTkBlock = 512;
 constexpr int kTkWaves = kTkBlock / 64;
 constexpr int kCap = 32768;   // keys cached in LDS (128 KiB)
 
+constexpr int kUnroll = 4;     // 16-byte loads in flight per thread
+
 __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
     if (u == 0x80000000u) u = 0u;                            // -0 -> +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);       // monotone in the real value
 }
 
+// f(i, key) for every position i < n of a score row in global memory (each i once, in no set order).
+template <typename F>
+__device__ __forceinline__ void for_each_raw(const float* __restrict__ srow, int n, bool vec, F&& f) {
+    const int tid = threadIdx.x;
+    if (!vec) {
+        for (int i = tid; i < n; i += kTkBlock) f(i, order_key(srow[i]));
+        return;
+    }
+    for (int base = 0; base < n; base += kTkBlock * 4 * kUnroll) {
+        float4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int i = base + 4 * (u * kTkBlock + tid);
+            if (i + 3 < n) {
+                v[u] = *(const float4*)(srow + i);
+            } else {
+                v[u].x = i < n ? srow[i] : 0.0f;
+                v[u].y = i + 1 < n ? srow[i + 1] : 0.0f;
+                v[u].z = i + 2 < n ? srow[i + 2] : 0.0f;
+                v[u].w = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int i = base + 4 * (u * kTkBlock + tid);
+            if (i < n) f(i, order_key(v[u].x));
+            if (i + 1 < n) f(i + 1, order_key(v[u].y));
+            if (i + 2 < n) f(i + 2, order_key(v[u].z));
+            if (i + 3 < n) f(i + 3, order_key(v[u].w));
+        }
+    }
+}
+
+// The same over the keys cached in LDS (16-byte reads; the cache is 16-byte aligned).
+template <typename F>
+__device__ __forceinline__ void for_each_cached(const uint32_t* keys, int n, F&& f) {
+    const int tid = threadIdx.x;
+    for (int i = 4 * tid; i < n; i += 4 * kTkBlock) {
+        const uint4 v = *(const uint4*)(keys + i);
+        f(i, v.x);
+        if (i + 1 < n) f(i + 1, v.y);
+        if (i + 2 < n) f(i + 2, v.z);
+        if (i + 3 < n) f(i + 3, v.w);
+    }
+}
+
 __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict__ scores, int64_t ld,
                                                         BatchView bv, int k, int32_t* __restrict__ out,
                                                         int cap) {
-    extern __shared__ uint32_t keys[];   // [cap]
-    __shared__ uint32_t hist[256];
+    extern __shared__ __align__(16) uint32_t keys[];   // [cap]
+    __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (fewer atomic collisions)
     __shared__ uint32_t red[2][kTkWaves];
     __shared__ uint32_t sel[2];
     __shared__ uint32_t wcnt[2][kTkWaves];
@@ -46,14 +94,15 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     const float* srow = scores + (int64_t)t * ld;
     const bool cached = n <= cap;
 
-    // keys (cached in LDS when the row fits) and their min / max
+    // keys (cached in LDS when the row fits) and their min / max; the row is read with 16-byte loads,
+    // kUnroll of them in flight per thread, when it is 16-byte aligned
+    const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int i = tid; i < n; i += kTkBlock) {
-        const uint32_t kk = order_key(srow[i]);
+    for_each_raw(srow, n, vec, [&](int i, uint32_t kk) {
         if (cached) keys[i] = kk;
         lo = min(lo, kk);
         hi = max(hi, kk);
-    }
+    });
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
     if (lane == 0) { red[0][wave] = lo; red[1][wave] = hi; }
@@ -76,17 +125,21 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
             const int width = min(8, pos + 1);
             const int shift = pos + 1 - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < 256; i += kTkBlock) hist[i] = 0u;
+            for (int i = tid; i < kTkWaves * 256; i += kTkBlock) (&hist[0][0])[i] = 0u;
             __syncthreads();
-            for (int i = tid; i < n; i += kTkBlock) {
-                const uint32_t kk = key_at(i);
-                if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1u);
-            }
+            auto count = [&](int, uint32_t kk) {
+                if ((kk & mask) == prefix) atomicAdd(&hist[wave][(kk >> shift) & dmask], 1u);
+            };
+            if (cached) for_each_cached(keys, n, count);
+            else for_each_raw(srow, n, vec, count);
             __syncthreads();
             if (wave == 0) {
                 // the digit d with (count above d) < remaining <= (count at or above d)
                 uint32_t cnt[4];
-                for (int j = 0; j < 4; j++) cnt[j] = hist[4 * lane + j];
+                for (int j = 0; j < 4; j++) {
+                    cnt[j] = 0u;
+                    for (int w = 0; w < kTkWaves; w++) cnt[j] += hist[w][4 * lane + j];
+                }
                 const uint32_t local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
                 uint32_t suf = local;                      // sum over lanes >= lane
                 for (int o = 1; o < 64; o <<= 1) {
@@ -156,7 +209,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int
                        hipStream_t st) {
     if (bv.T == 0) return hipSuccess;
     const int cap = bv.max_len > k ? min(bv.max_len, kCap) : 0;
-    const size_t shm = (size_t)cap * sizeof(uint32_t);
+    const size_t shm = (size_t)((cap + 3) & ~3) * sizeof(uint32_t);   // whole 16-byte reads stay inside
     if (shm > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)shm);
