@@ -46,7 +46,7 @@ constexpr int kRowB = kRowSlots * 16;           // 1168 bytes
 constexpr int kTileSlots = kTile * kRowSlots;   // 2336 16-byte LDS slots per tile
 constexpr int kLoadsPerWave = (kTileSlots + kMlaThreads - 1) / kMlaThreads;
 constexpr int kMaxList = 2048;                  // index slots per split
-constexpr int kAhead = 4;                       // logit operand reads in flight
+constexpr int kAhead = 2;                       // logit operand reads in flight
 constexpr int kAheadV = 2;                      // value operand steps in flight
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kHeadroom = 64.0f;              // log2 margin above a head's reference max
@@ -56,6 +56,20 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// Workgroup barrier for the main loop: waits for this wave's own LDS operations only.
+// __syncthreads() also carries a release fence, which makes the compiler drain every outstanding
+// vector-memory operation (vmcnt(0)) -- including the global->LDS tile loads kept in flight on
+// purpose.  Tile completion is handled explicitly (s_waitcnt vmcnt(N) before the barrier), so the
+// loop needs only the LDS ordering.  The "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+// Byte offset of an LDS object, as ds_* instructions address it.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* p0, const uint8_t* p1) {
     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
@@ -75,6 +89,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][4][64];   // partial-logit exchange
     __shared__ int32_t rows[kMaxList];
     __shared__ int wcount[kMlaWaves];
+    __shared__ bf16x8 qlast[kMlaWaves][64];   // the last query fragment of each lane (see below)
 
     // XCD-aware order: consecutive workgroups go to different XCDs (round robin over 8), so the
     // splits of one query take block ids 8 apart and share that XCD's L2 for the query block.
@@ -95,13 +110,18 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // lane (g, c32) holds head 32*hg + c32, dims 288*half + 16*kk + 8*g + [0, 8)
     const int hq = kHeadsPerGroup * hg + c32;
     const bool wave_on = kHeadsPerGroup * hg < H;
-    bf16x8 qf[kQkHalf / 16];
+    // The last of the 18 fragments is parked in LDS (read back once per tile): with all 18 in
+    // VGPRs the loop needs one register more than the 256 it has at two waves per SIMD, and a
+    // scratch reload would wait for the tile loads in flight.
+    constexpr int kQf = kQkHalf / 16;
+    bf16x8 qf[kQf - 1];
     const bf16x8 zero8 = {};
+    const bool q_on = wave_on && hq < H;
+    const uint16_t* qrow = q + ((int64_t)t * H + hq) * kDqk + kQkHalf * half + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < kQkHalf / 16; kk++)
-        qf[kk] = (wave_on && hq < H)
-                     ? *(const bf16x8*)(q + ((int64_t)t * H + hq) * kDqk + kQkHalf * half + 16 * kk + 8 * g)
-                     : zero8;
+    for (int kk = 0; kk < kQf - 1; kk++) qf[kk] = q_on ? *(const bf16x8*)(qrow + 16 * kk) : zero8;
+    qlast[wave][lane] = q_on ? *(const bf16x8*)(qrow + 16 * (kQf - 1)) : zero8;
+    const uint32_t qlast_addr = lds_addr(&qlast[wave][lane]);
 
     // 0. compact the valid selected positions of this split into storage rows
     int cnt = 0;
@@ -131,10 +151,14 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int my_loads = (kTileSlots - wave_u * 64 + kMlaThreads - 1) / kMlaThreads;   // instructions per tile
     auto load_tile = [&](int tile, uint8_t* tb) {
+        // the lane number passes through an empty asm so that the per-lane slot arithmetic below is
+        // redone at each call instead of being hoisted into registers that stay live all loop long
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
 #pragma unroll
         for (int r = 0; r < kLoadsPerWave; r++) {
             const int p0 = (r * kMlaWaves + wave_u) * 64;
-            const int p = p0 + lane;
+            const int p = p0 + lane_o;
             if (p < kTileSlots) {
                 const int rr = p / kRowSlots, cc = p - rr * kRowSlots;
                 if (cc < kRowChunks) {
@@ -175,6 +199,10 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     //    8*(i/4) + 4*g + i%4 of the tile for head c32
     auto qk_tile = [&](const uint8_t* tb) -> f32x16 {
         f32x16 sacc = {};
+        // the parked query fragment; read in asm, with its wait, so the compiler does not hold the
+        // read back for the tile loads in flight
+        bf16x8 ql;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(ql) : "v"(qlast_addr) : "memory");
         const uint8_t* rp = tb + c32 * kRowB + 16 * g + 2 * kQkHalf * half;
         bf16x8 kb[kAhead];
 #pragma unroll
@@ -183,7 +211,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int kk = 0; kk < kQkHalf / 16; kk++) {
             const bf16x8 a = kb[kk % kAhead];
             if (kk + kAhead < kQkHalf / 16) kb[kk % kAhead] = *(const bf16x8*)(rp + 32 * (kk + kAhead));
-            sacc = mfma32(a, qf[kk], sacc);
+            sacc = mfma32(a, kk < kQf - 1 ? qf[kk] : ql, sacc);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
@@ -196,18 +224,33 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     };
     // the two halves' partial logits -> full (unscaled) logits; IEEE addition is commutative, so
     // both waves of the pair get bit-identical sums.  Keys past the end of the list (last tile
-    // only) are masked to -inf.
-    auto logits = [&](int tile, const f32x16& part, float (&z)[16]) -> float {
-        f32x4* mine = &sx[wave][0][lane];
-#pragma unroll
-        for (int u = 0; u < 4; u++) mine[64 * u] = f32x4{part[4 * u], part[4 * u + 1], part[4 * u + 2], part[4 * u + 3]};
-        __syncthreads();
+    // only) are masked to -inf.  The writes and the barrier are one asm block: written in C++, the
+    // compiler may make the writes wait for every tile load in flight (it cannot always tell that
+    // `sx` is not their destination).
+    const uint32_t sx_mine = lds_addr(&sx[wave][0][lane]);
+    auto logits = [&](int tile, f32x16& z) -> float {   // z: this wave's partial logits in, full logits out
+        // z comes straight from the MFMA chain; the hazard padding the compiler adds before its own
+        // reads of an MFMA result is not applied to inline asm, so the block starts with 20 wait
+        // states itself (more than any MFMA result needs before an LDS instruction reads it).
+        asm volatile(
+            "s_nop 15\n\t"
+            "s_nop 3\n\t"
+            "ds_write_b128 %0, %1\n\t"
+            "ds_write_b128 %0, %2 offset:1024\n\t"
+            "ds_write_b128 %0, %3 offset:2048\n\t"
+            "ds_write_b128 %0, %4 offset:3072\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "s_barrier" ::"v"(sx_mine), "v"(f32x4{z[0], z[1], z[2], z[3]}), "v"(f32x4{z[4], z[5], z[6], z[7]}),
+            "v"(f32x4{z[8], z[9], z[10], z[11]}), "v"(f32x4{z[12], z[13], z[14], z[15]}) : "memory");
         const f32x4* other = &sx[wave ^ 1][0][lane];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const f32x4 o = other[64 * u];
 #pragma unroll
-            for (int e = 0; e < 4; e++) z[4 * u + e] = part[4 * u + e] + o[e];
+            for (int e = 0; e < 4; e++) z[4 * u + e] += o[e];
+            // half the partner's values at a time: fewer live registers at this point keeps the
+            // query block out of scratch (a reload would wait for the tile loads in flight)
+            if (u == 1) __builtin_amdgcn_sched_barrier(0);
         }
         if ((tile + 1) * kTile > cnt) {
 #pragma unroll
@@ -222,7 +265,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // 4. O[heads 8(i/4) + 4g + i%4][dims 256*half + 32nd + c32] += P V.  Step m covers keys
     //    16m + 8(r/4) + 4g + r%4 in k-slot r; the two transpose reads fetch rows 16m + 4g + [0,4)
     //    and 16m + 8 + 4g + [0,4).
-    auto pv_tile = [&](f32x16 (&acc)[kVHalf / 32], const uint8_t* tb, const float (&z)[16], float mref) {
+    auto pv_tile = [&](f32x16 (&acc)[kVHalf / 32], const uint8_t* tb, const f32x16& z, float mref) {
         bf16x8 pf[2];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -267,9 +310,12 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     //    Every wave takes part in the exchange barrier, also waves without heads.
     bool over = false;
     auto fast_tile = [&](int tile, const uint8_t* tb) {
-        const f32x16 part = wave_on ? qk_tile(tb) : f32x16{};
-        float z[16];
-        const float mt = logits(tile, part, z);
+        // every wave runs the QK step (a wave without heads holds a zero query block); the fences
+        // keep the scheduler from stretching register lifetimes across it
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 z = qk_tile(tb);
+        __builtin_amdgcn_sched_barrier(0);
+        const float mt = logits(tile, z);
         if (!wave_on) return;
         if (tile == 0) m_run = mt;
         over |= mt > m_run + kHeadroom;
@@ -277,23 +323,23 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     };
 
     wait_ahead(true, ntiles > 1);
-    __syncthreads();
+    lds_barrier();
     for (int tile = 0; tile < ntiles; tile += 3) {
         // tile i is consumed while tiles i+1 (issued earlier) and i+2 (issued now) are in flight
         if (tile + 2 < ntiles) load_tile(tile + 2, tile_c);
         fast_tile(tile, tile_a);
         wait_ahead(tile + 1 < ntiles, tile + 2 < ntiles);
-        __syncthreads();
+        lds_barrier();
         if (tile + 1 >= ntiles) break;
         if (tile + 3 < ntiles) load_tile(tile + 3, tile_a);
         fast_tile(tile + 1, tile_b);
         wait_ahead(tile + 2 < ntiles, tile + 3 < ntiles);
-        __syncthreads();
+        lds_barrier();
         if (tile + 2 >= ntiles) break;
         if (tile + 4 < ntiles) load_tile(tile + 4, tile_b);
         fast_tile(tile + 2, tile_c);
         wait_ahead(tile + 3 < ntiles, tile + 4 < ntiles);
-        __syncthreads();
+        lds_barrier();
     }
 
     // 5. normalise and store (bf16 output when the split is the whole selection, else bf16 partials)
@@ -349,9 +395,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         load_tile(tile, tile_a);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        const f32x16 part = wave_on ? qk_tile(tile_a) : f32x16{};
-        float z[16];
-        m_exact = fmaxf(m_exact, logits(tile, part, z));
+        f32x16 z = wave_on ? qk_tile(tile_a) : f32x16{};
+        m_exact = fmaxf(m_exact, logits(tile, z));
     }
     f32x16 acc2[kVHalf / 32];
 #pragma unroll
@@ -362,9 +407,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         load_tile(tile, tile_a);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        const f32x16 part = wave_on ? qk_tile(tile_a) : f32x16{};
-        float z[16];
-        logits(tile, part, z);
+        f32x16 z = wave_on ? qk_tile(tile_a) : f32x16{};
+        logits(tile, z);
         if (wave_on) pv_tile(acc2, tile_a, z, m_exact);
     }
     finish(acc2, l_run, m_exact);
