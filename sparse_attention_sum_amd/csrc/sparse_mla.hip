@@ -155,14 +155,20 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // redone at each call instead of being hoisted into registers that stay live all loop long
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
+        const int rbase = tile * kTile, last = cnt - 1;
 #pragma unroll
         for (int r = 0; r < kLoadsPerWave; r++) {
+            // slot p = p0 + lane: row p / 73, chunk p % 73, from the wave-uniform split of p0 plus
+            // at most one wrap (lane < 64 < 73)
             const int p0 = (r * kMlaWaves + wave_u) * 64;
-            const int p = p0 + lane_o;
-            if (p < kTileSlots) {
-                const int rr = p / kRowSlots, cc = p - rr * kRowSlots;
+            const int rr0 = p0 / kRowSlots, cc0 = p0 - rr0 * kRowSlots;
+            const int c = cc0 + lane_o;
+            const bool wrap = c >= kRowSlots;
+            const int cc = wrap ? c - kRowSlots : c;
+            const int rr = rr0 + (wrap ? 1 : 0);
+            if (p0 + lane_o < kTileSlots) {
                 if (cc < kRowChunks) {
-                    const int row = rows[min(tile * kTile + rr, cnt - 1)];
+                    const int row = rows[min(rbase + rr, last)];
                     const uint8_t* src = (const uint8_t*)lat.data + (int64_t)row * (kDqk * 2) + cc * 16;
                     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                                      (__attribute__((address_space(3))) void*)(tb + p0 * 16), 16, 0, 0);
