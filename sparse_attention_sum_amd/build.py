@@ -27,18 +27,44 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-file flags for the device (gfx950) compilation only.  The sparse-MLA main loop holds a 32x288
+# query block and a 32x256 output block in registers at two waves per SIMD, with only a few
+# registers to spare; the register-minimising machine scheduler keeps it free of spill reloads (a
+# reload there would wait for the tile loads in flight).  LLVM options given to hipcc reach the
+# host compilation too, so such files are built in three steps: device code object, offload
+# bundle, host object embedding the bundle.
+DEVICE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-misched=gcn-iterative-minreg"]}
+BUNDLER = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang-offload-bundler")
+if not os.path.exists(BUNDLER):
+    BUNDLER = "/opt/rocm/llvm/bin/clang-offload-bundler"
 
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+def _run(cmd, what):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"{what} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+
+def _compile(src: str, extra) -> str:
+    name = os.path.basename(src)
+    obj = os.path.join(BUILD, name + ".o")
+    dev = DEVICE_FLAGS.get(name)
+    if dev is None:
+        _run([HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj], f"hipcc {name}")
+        return obj
+    code = os.path.join(BUILD, name + ".co")
+    bundle = os.path.join(BUILD, name + ".hipfb")
+    _run([HIPCC, *CFLAGS, *dev, *extra, "--cuda-device-only", "--no-gpu-bundle-output", "-c", src, "-o", code],
+         f"hipcc (device) {name}")
+    _run([BUNDLER, "-type=o", "-bundle-align=4096",
+          f"-targets=host-x86_64-unknown-linux-gnu,hipv4-amdgcn-amd-amdhsa--{ARCH}",
+          "-input=/dev/null", f"-input={code}", f"-output={bundle}"], f"bundle {name}")
+    _run([HIPCC, *CFLAGS, *extra, "--cuda-host-only", "-Xclang", "-fcuda-include-gpubinary", "-Xclang", bundle,
+          "-c", src, "-o", obj], f"hipcc (host) {name}")
     return obj
 
 

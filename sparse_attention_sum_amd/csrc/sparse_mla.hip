@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][4][64];   // partial-logit exchange
     __shared__ int32_t rows[kMaxList];
     __shared__ int wcount[kMlaWaves];
+    __shared__ int xflag[kMlaWaves];   // per wave: number of partial-logit blocks published in sx
     __shared__ bf16x8 qlast[kMlaWaves][64];   // the last query fragment of each lane (see below)
 
     // XCD-aware order: consecutive workgroups go to different XCDs (round robin over 8), so the
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int n = seq_ok ? min(bv.q_len[t], bv.max_len) : 0;
     const int j0 = split * per_split, j1 = min(k, j0 + per_split);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
+    if (lane == 0) xflag[wave] = 0;
 
     // query half-block (loads issued first, so their latency overlaps the index compaction):
     // lane (g, c32) holds head 32*hg + c32, dims 288*half + 16*kk + 8*g + [0, 8)
@@ -230,10 +232,17 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     };
     // the two halves' partial logits -> full (unscaled) logits; IEEE addition is commutative, so
     // both waves of the pair get bit-identical sums.  Keys past the end of the list (last tile
-    // only) are masked to -inf.  The writes and the barrier are one asm block: written in C++, the
-    // compiler may make the writes wait for every tile load in flight (it cannot always tell that
-    // `sx` is not their destination).
+    // only) are masked to -inf.
+    // Only the two waves of a pair meet here: each publishes its partial block in sx and then bumps
+    // its own counter in xflag; the partner waits for that count.  (A workgroup barrier here would
+    // lock all eight waves into the same phase.)  The end-of-tile barrier orders the next write of
+    // sx after the partner's read of this one.  The writes are one asm block: written in C++, the
+    // compiler may make them wait for every tile load in flight (it cannot always tell that `sx` is
+    // not their destination); the flag is read in asm for the same reason.
     const uint32_t sx_mine = lds_addr(&sx[wave][0][lane]);
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar addresses
+    const uint32_t flag_mine = lds_addr(&xflag[wave_s]), flag_other = lds_addr(&xflag[wave_s ^ 1]);
+    int xepoch = 0;
     auto logits = [&](int tile, f32x16& z) -> float {   // z: this wave's partial logits in, full logits out
         // z comes straight from the MFMA chain; the hazard padding the compiler adds before its own
         // reads of an MFMA result is not applied to inline asm, so the block starts with 20 wait
@@ -246,8 +255,19 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
             "ds_write_b128 %0, %3 offset:2048\n\t"
             "ds_write_b128 %0, %4 offset:3072\n\t"
             "s_waitcnt lgkmcnt(0)\n\t"
-            "s_barrier" ::"v"(sx_mine), "v"(f32x4{z[0], z[1], z[2], z[3]}), "v"(f32x4{z[4], z[5], z[6], z[7]}),
-            "v"(f32x4{z[8], z[9], z[10], z[11]}), "v"(f32x4{z[12], z[13], z[14], z[15]}) : "memory");
+            "ds_write_b32 %5, %6\n\t"
+            "s_waitcnt lgkmcnt(0)" ::"v"(sx_mine), "v"(f32x4{z[0], z[1], z[2], z[3]}), "v"(f32x4{z[4], z[5], z[6], z[7]}),
+            "v"(f32x4{z[8], z[9], z[10], z[11]}), "v"(f32x4{z[12], z[13], z[14], z[15]}), "v"(flag_mine),
+            "v"(xepoch + 1) : "memory");
+        xepoch++;
+        // bounded wait for the partner (both waves of a pair run the same sequence of exchanges,
+        // so the count always arrives; the bound only keeps a broken invariant from hanging)
+        for (int spin = 0; spin < (1 << 22); spin++) {
+            int f;
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(flag_other) : "memory");
+            if (__builtin_amdgcn_readfirstlane(f) >= xepoch) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
         const f32x4* other = &sx[wave ^ 1][0][lane];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
