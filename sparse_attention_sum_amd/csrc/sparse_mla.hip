@@ -441,58 +441,74 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // Merge the splits of each (query, head) with weights exp(lse_s - lse), in a fixed order over s.
-// One workgroup per (query, wave slot) = 32 heads x 256 dims: the weights of the slot's heads are
-// computed once into LDS, then each thread folds 16-byte chunks of the splits' partials.
+// One workgroup per (query, head group of 32, part of the group's partial block); a thread merges
+// one 16-byte chunk.  S (the split count) is a template argument for the common counts, so a
+// thread issues all S loads before it uses the first; the weights of the group's heads are
+// computed into LDS by each workgroup (32 x S small loads).
 constexpr int kCombThreads = 256;
 constexpr int kMaxSplitsComb = 64;
+constexpr int kCombChunks = kHeadsPerGroup * kDv / 8;         // 16-byte chunks per head group
+constexpr int kCombParts = kCombChunks / kCombThreads;        // workgroups per (query, group)
 
+template <int S>   // S > 0: compile-time split count; S == 0: runtime count `splits`
 __global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                    const float* __restrict__ part_lse, int splits,
                                                                    int H, int T, uint16_t* __restrict__ out,
                                                                    float* __restrict__ lse) {
     __shared__ float wts[kMaxSplitsComb][kHeadsPerGroup];
+    const int ns = S > 0 ? S : splits;
     const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;   // padded heads
-    const int nslots = hp / kHeadsPerGroup * 2;
-    const int t = blockIdx.x / nslots, slot = blockIdx.x % nslots;
-    const int hg = slot >> 1, half = slot & 1;
+    const int ngroups = hp / kHeadsPerGroup;
+    const int part = blockIdx.x % kCombParts;
+    const int t = blockIdx.x / kCombParts / ngroups, hg = blockIdx.x / kCombParts % ngroups;
     const int tid = threadIdx.x;
+    // chunk c (16 bytes = 8 bf16) of the group: row rho = c/32 (nd = rho/4, ig = rho%4), partial
+    // lanes L = 2*(c%32) and L+1, each with 4 consecutive heads 8*ig + 4*(L/32) + e at dims
+    // 32*nd + L%32 (+1)
+    const int c = part * kCombThreads + tid;
+    const uint16_t* src = part_o + (int64_t)t * ns * hp * kDv + (int64_t)hg * kHeadsPerGroup * kDv + 8 * c;
+    const int64_t sstride = (int64_t)hp * kDv;
+    i32x4 raw[S > 0 ? S : 1];
+    if constexpr (S > 0) {
+#pragma unroll
+        for (int s = 0; s < S; s++) raw[s] = *(const i32x4*)(src + s * sstride);
+    }
     if (tid < kHeadsPerGroup) {
         const int head = kHeadsPerGroup * hg + tid;
-        const float* pl = part_lse + (int64_t)t * splits * hp + head;
+        const float* pl = part_lse + (int64_t)t * ns * hp + head;
         float m = -INFINITY;
-        for (int s = 0; s < splits; s++) m = fmaxf(m, pl[(int64_t)s * hp]);
+        for (int s = 0; s < ns; s++) m = fmaxf(m, pl[(int64_t)s * hp]);
         float wsum = 0.0f;
-        for (int s = 0; s < splits; s++) wsum += m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m);
+        for (int s = 0; s < ns; s++) wsum += m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m);
         const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-        for (int s = 0; s < splits; s++) wts[s][tid] = m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m) * inv;
-        if (lse && half == 0 && head < H) lse[(int64_t)t * H + head] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
+        for (int s = 0; s < ns; s++) wts[s][tid] = m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m) * inv;
+        if (lse && part == 0 && head < H) lse[(int64_t)t * H + head] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
     }
     __syncthreads();
-    // chunk c (16 bytes = 8 bf16) of the slot: row rho = c/32 (nd = rho/4, ig = rho%4), partial lanes
-    // L = 2*(c%32) and L+1, each with 4 consecutive heads 8*ig + 4*(L/32) + e at dims 32*nd + L%32 (+1)
-    constexpr int kChunks = kHeadsPerGroup * kVHalf / 8;
-    for (int c = tid; c < kChunks; c += kCombThreads) {
-        const int rho = c >> 5, nd = rho >> 2, ig = rho & 3, L = 2 * (c & 31);
-        const int hl0 = 8 * ig + 4 * (L >> 5);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; s++) {
-            const i32x4 raw = *(const i32x4*)(part_o + ((int64_t)t * splits + s) * hp * kDv +
-                                              (int64_t)slot * kHeadsPerGroup * kVHalf + 8 * c);
+    const int rho = c >> 5, nd = rho >> 2, ig = rho & 3, L = 2 * (c & 31);
+    const int hl0 = 8 * ig + 4 * (L >> 5);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](const i32x4& r, int s) {
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const uint32_t wd = (uint32_t)raw[e / 2];
-                const float v = bf16_bits_to_f32((uint16_t)(e % 2 ? wd >> 16 : wd & 0xffff));
-                acc[e] = fmaf(wts[s][hl0 + (e % 4)], v, acc[e]);
-            }
+        for (int e = 0; e < 8; e++) {
+            const uint32_t wd = (uint32_t)r[e / 2];
+            const float v = bf16_bits_to_f32((uint16_t)(e % 2 ? wd >> 16 : wd & 0xffff));
+            acc[e] = fmaf(wts[s][hl0 + (e % 4)], v, acc[e]);
         }
-        const int dim = kVHalf * half + 32 * nd + (L & 31);
+    };
+    if constexpr (S > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int head = kHeadsPerGroup * hg + hl0 + e;
-            if (head < H) {
-                const uint32_t pair = (uint32_t)f32_to_bf16_bits(acc[e]) | ((uint32_t)f32_to_bf16_bits(acc[4 + e]) << 16);
-                *(uint32_t*)(out + ((int64_t)t * H + head) * kDv + dim) = pair;
-            }
+        for (int s = 0; s < S; s++) fold(raw[s], s);
+    } else {
+        for (int s = 0; s < ns; s++) fold(*(const i32x4*)(src + s * sstride), s);
+    }
+    const int dim = 32 * nd + (L & 31);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int head = kHeadsPerGroup * hg + hl0 + e;
+        if (head < H) {
+            const uint32_t pair = (uint32_t)f32_to_bf16_bits(acc[e]) | ((uint32_t)f32_to_bf16_bits(acc[4 + e]) << 16);
+            *(uint32_t*)(out + ((int64_t)t * H + head) * kDv + dim) = pair;
         }
     }
 }
@@ -537,8 +553,14 @@ hipError_t launch_sparse_mla(const uint16_t* q, int H, const CacheView& lat, con
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;
-    const int blocks = bv.T * (hp / kHeadsPerGroup) * 2;
-    mla_combine_kernel<<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse);
+    const int blocks = bv.T * (hp / kHeadsPerGroup) * kCombParts;
+    switch (splits) {
+        case 2: mla_combine_kernel<2><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        case 3: mla_combine_kernel<3><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        case 4: mla_combine_kernel<4><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        case 8: mla_combine_kernel<8><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        default: mla_combine_kernel<0><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+    }
     return hipGetLastError();
 }
 

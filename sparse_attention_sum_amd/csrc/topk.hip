@@ -6,11 +6,13 @@
 //
 // One workgroup per query row.  Scores map to order-preserving unsigned keys (-0 is folded onto
 // +0 first, so equal reals give equal keys).  A radix select finds the exact k-th largest key
-// `thr`: the bits above the common prefix of the row's min and max key are skipped, then 8-bit
+// `thr`: the bits above the common prefix of the row's min and max key are skipped, then 11-bit
 // digits are resolved with LDS histograms, each pass keeping only keys that match the prefix found
-// so far.  A final ordered compaction writes every key > thr plus the lowest-position keys == thr,
-// in ascending position order, which makes the output deterministic.  Rows of up to kCap scores
-// are cached in LDS; longer rows are re-read from global memory (L2) on each pass.
+// so far.  The passes stop early once the bin holding the k-th key is needed whole (usually after
+// two passes).  A final ordered compaction writes every key above the threshold plus the
+// lowest-position keys equal to it (compared on the resolved bits), in ascending position order,
+// which makes the output deterministic.  Rows of up to kCap scores are cached in LDS; longer rows
+// are re-read from global memory (L2) on each pass.
 #include "kernels.h"
 
 namespace dsa {
@@ -21,6 +23,9 @@ constexpr int kTkWaves = kTkBlock / 64;
 constexpr int kCap = 32768;   // keys cached in LDS (128 KiB)
 
 constexpr int kUnroll = 4;     // 16-byte loads in flight per thread
+constexpr int kDigitBits = 11; // radix digit width
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kHistCopies = 2;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __float_as_uint(x);
@@ -78,9 +83,9 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
                                                         BatchView bv, int k, int32_t* __restrict__ out,
                                                         int cap) {
     extern __shared__ __align__(16) uint32_t keys[];   // [cap]
-    __shared__ uint32_t hist[kTkWaves][256];   // one histogram per wave (fewer atomic collisions)
+    __shared__ uint32_t hist[kHistCopies][kBins];   // copies shared by alternate waves (fewer collisions)
     __shared__ uint32_t red[2][kTkWaves];
-    __shared__ uint32_t sel[2];
+    __shared__ uint32_t sel[3];
     __shared__ uint32_t wcnt[2][kTkWaves];
 
     const int t = blockIdx.x;
@@ -122,53 +127,66 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
         prefix = lo & mask;
         int pos = top;
         while (pos >= 0) {
-            const int width = min(8, pos + 1);
+            const int width = min(kDigitBits, pos + 1);
             const int shift = pos + 1 - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < kTkWaves * 256; i += kTkBlock) (&hist[0][0])[i] = 0u;
+            for (int i = tid; i < kHistCopies * kBins; i += kTkBlock) (&hist[0][0])[i] = 0u;
             __syncthreads();
+            uint32_t* myhist = hist[wave % kHistCopies];
             auto count = [&](int, uint32_t kk) {
-                if ((kk & mask) == prefix) atomicAdd(&hist[wave][(kk >> shift) & dmask], 1u);
+                if ((kk & mask) == prefix) atomicAdd(&myhist[(kk >> shift) & dmask], 1u);
             };
             if (cached) for_each_cached(keys, n, count);
             else for_each_raw(srow, n, vec, count);
             __syncthreads();
-            if (wave == 0) {
-                // the digit d with (count above d) < remaining <= (count at or above d)
-                uint32_t cnt[4];
-                for (int j = 0; j < 4; j++) {
-                    cnt[j] = 0u;
-                    for (int w = 0; w < kTkWaves; w++) cnt[j] += hist[w][4 * lane + j];
+            {
+                // the digit d with (count above d) < remaining <= (count at or above d): thread t
+                // owns bins [4t, 4t + 4); a suffix scan over the block gives the keys above them
+                constexpr int kPerThread = kBins / kTkBlock;
+                uint32_t c[kPerThread], local = 0u;
+#pragma unroll
+                for (int j = 0; j < kPerThread; j++) {
+                    c[j] = 0u;
+#pragma unroll
+                    for (int h = 0; h < kHistCopies; h++) c[j] += hist[h][kPerThread * tid + j];
+                    local += c[j];
                 }
-                const uint32_t local = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-                uint32_t suf = local;                      // sum over lanes >= lane
+                uint32_t suf = local;                      // sum over this wave's lanes >= lane
                 for (int o = 1; o < 64; o <<= 1) {
                     const uint32_t v = __shfl_down(suf, o, 64);
                     if (lane + o < 64) suf += v;
                 }
-                uint32_t acc = suf - local;                // keys in bins above this lane's bins
-                if (acc < remaining && remaining <= suf) {
-                    for (int j = 3; j >= 0; j--) {
-                        if (remaining <= acc + cnt[j]) {
-                            sel[0] = 4 * lane + j;
+                if (lane == 0) red[0][wave] = suf;
+                __syncthreads();
+                uint32_t acc = suf - local;                // keys in bins above this thread's bins
+                for (int w = wave + 1; w < kTkWaves; w++) acc += red[0][w];
+                if (acc < remaining && remaining <= acc + local) {
+#pragma unroll
+                    for (int j = kPerThread - 1; j >= 0; j--) {
+                        if (remaining <= acc + c[j]) {
+                            sel[0] = kPerThread * tid + j;
                             sel[1] = acc;
+                            sel[2] = c[j];
                             break;
                         }
-                        acc += cnt[j];
+                        acc += c[j];
                     }
                 }
             }
             __syncthreads();
-            const uint32_t d = sel[0], above = sel[1];
+            const uint32_t d = sel[0], above = sel[1], inbin = sel[2];
             remaining -= above;
             prefix |= d << shift;
             mask |= dmask << shift;
             pos = shift - 1;
             __syncthreads();
+            // every key of this bin is needed: the selection is settled without the lower bits
+            if (inbin == remaining) break;
         }
     }
-    // `prefix` is now the k-th largest key: all keys above it are taken, and the `remaining`
-    // lowest-position keys equal to it.
+    // On the resolved bits (`mask`), `prefix` is now the k-th largest key: all keys above it are
+    // taken, and the `remaining` lowest-position keys equal to it (all of them after an early
+    // exit, where the bin holds exactly `remaining` keys).
     const uint32_t thr = prefix, need_eq = remaining;
 
     // ordered compaction: wave w owns positions [beg, end), in steps of 64
@@ -177,7 +195,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     uint32_t cgt = 0, ceq = 0;
     for (int base = beg; base < end; base += 64) {
         const int i = base + lane;
-        const uint32_t kk = i < end ? key_at(i) : 0u;
+        const uint32_t kk = i < end ? key_at(i) & mask : 0u;
         cgt += __popcll(__ballot(i < end && kk > thr));
         ceq += __popcll(__ballot(i < end && kk == thr));
     }
@@ -190,7 +208,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = beg; base < end; base += 64) {
         const int i = base + lane;
-        const uint32_t kk = i < end ? key_at(i) : 0u;
+        const uint32_t kk = i < end ? key_at(i) & mask : 0u;
         const bool gt = i < end && kk > thr;
         const bool eq = i < end && kk == thr;
         const uint64_t beq = __ballot(eq);
