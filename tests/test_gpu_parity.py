@@ -230,6 +230,10 @@ def test_topk_stress_rows():
     v = rng.standard_normal(5000).astype(np.float32); v[::2] = -np.inf     # -inf entries
     add(v)
     add(np.concatenate([np.full(100, 3.0), np.full(4000, 2.0)]).astype(np.float32))  # threshold inside a tie run
+    # rows longer than the LDS key cache: candidates gathered into LDS (integer ties at the
+    # threshold), and a tie run at the threshold larger than the candidate area (global fallback)
+    add(rng.integers(0, 100, 36000).astype(np.float32))
+    add(np.concatenate([np.full(20000, 0.5), np.full(20000, 1.0)]).astype(np.float32)[rng.permutation(40000)])
     S = np.stack(rows)
     q_len = np.array(lens, np.int32)
     T = len(lens)
