@@ -87,17 +87,20 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, f32x1
 }
 
 // QG query tokens of one sequence share each key fetch (1 for plain decode, 2 for two-token
-// speculative decode).  A wave keeps PF key subtiles (32 keys each) in flight: the loads of subtile
-// i + PF are issued as soon as subtile i has been consumed, so the wave never waits for HBM latency
-// more than once per PF subtiles.  Loads past the end of the context are clamped to its last token
-// (in bounds; their scores are not stored), which keeps the loop free of branches around loads.
+// speculative decode).  A wave keeps PF key subtiles (32 keys each) in flight (4, or 3 for QG = 2): the loads of subtile
+// i + PF are issued as soon as subtile i has been consumed.  The storage rows of all of the wave's
+// subtiles are looked up first (one batch of page-table loads), so a key load never waits for its
+// page lookup.  The head weights of a pass live in a per-wave LDS area (read 4 at a time where
+// they are used), which keeps registers for the key ring.  Loads past the end of the context are
+// clamped to its last token (in bounds; their scores are not stored).
 template <int NHS, int QG>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
     constexpr int H = 32 * NHS;
-    constexpr int PF = QG == 1 ? 4 : 2;
+    constexpr int PF = QG == 1 ? 4 : 3;   // two queries need more registers: one subtile less
     constexpr int kSub = kDecKeysPerWave / 32;
+    __shared__ __attribute__((aligned(16))) float wsh[kDecWaves][QG][H];   // w * q_scale, per wave
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
@@ -119,25 +122,35 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
         for (int u = 1; u < QG; u++) nmax = max(nmax, n[u]);
         if (key0 >= nmax) continue;
 
-        // key subtile ring: lane (g, c) holds dims 64g..64g+63 of key key0 + 32*sub + c
+        // storage rows of the wave's subtiles: lane (g, c) reads key key0 + 32*sub + c
+        uint32_t rowv[kSub];
+        uint32_t okm = 0;                  // bit sub: the key's page is valid
+#pragma unroll
+        for (int sub = 0; sub < kSub; sub++) {
+            const int64_t row = cache_row(kc, b, min<int64_t>(key0 + 32 * sub + c, nmax - 1));
+            rowv[sub] = row >= 0 ? (uint32_t)row : 0u;
+            okm |= row >= 0 ? (1u << sub) : 0u;
+        }
         i32x8 kf[PF][2];
         float ks[PF];
-        bool kv[PF];
         auto load_keys = [&](int j, int sub) {
-            const int64_t s = min<int64_t>(key0 + 32 * sub + c, nmax - 1);
-            const int64_t row = cache_row(kc, b, s);
-            kv[j] = row >= 0;
-            const int64_t r = row >= 0 ? row : 0;
-            const uint8_t* src = (const uint8_t*)kc.data + r * kIdxDim + 64 * g;
+            const uint8_t* src = (const uint8_t*)kc.data + (int64_t)rowv[sub] * kIdxDim + 64 * g;
             kf[j][0] = *(const i32x8*)(src);
             kf[j][1] = *(const i32x8*)(src + 32);
-            ks[j] = kc.scale ? kc.scale[r] : 1.0f;
+            ks[j] = kc.scale ? kc.scale[rowv[sub]] : 1.0f;
         };
 #pragma unroll
         for (int j = 0; j < PF; j++) load_keys(j, j);
 
+        // this pass's weights into the wave's own LDS area (no other wave reads it)
+#pragma unroll
+        for (int u = 0; u < QG; u++)
+            for (int r = lane; r < H; r += 64) {
+                const int t = t0 + (u < nq ? u : 0);
+                const float sc = q_scale ? q_scale[(int64_t)t * H + r] : 1.0f;
+                wsh[wave][u][r] = u < nq ? w[(int64_t)t * H + r] * sc : 0.0f;
+            }
         i32x8 qf[QG][NHS][2];
-        float wr[QG][NHS][16];
 #pragma unroll
         for (int u = 0; u < QG; u++) {
             const int t = t0 + (u < nq ? u : 0);
@@ -146,24 +159,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
                 const uint8_t* src = q + ((int64_t)t * H + 32 * hs + c) * kIdxDim + 64 * g;
                 qf[u][hs][0] = *(const i32x8*)(src);
                 qf[u][hs][1] = *(const i32x8*)(src + 32);
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * hs + 8 * (i / 4) + 4 * g + (i % 4);
-                    const float sc = q_scale ? q_scale[(int64_t)t * H + r] : 1.0f;
-                    wr[u][hs][i] = w[(int64_t)t * H + r] * sc;
-                }
             }
         }
 
 #pragma unroll
         for (int sub = 0; sub < kSub; sub++) {
             const int j = sub % PF;
-            const int64_t sb = key0 + 32 * sub;
-            const int64_t s = sb + c;
+            const int64_t s = key0 + 32 * sub + c;
             // an invalid page reads as an all-zero row
+            const bool ok = (okm >> sub) & 1u;
             const i32x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-            const i32x8 k0 = kv[j] ? kf[j][0] : zero, k1 = kv[j] ? kf[j][1] : zero;
-            const float ksj = kv[j] ? ks[j] : 0.0f;
+            const i32x8 k0 = ok ? kf[j][0] : zero, k1 = ok ? kf[j][1] : zero;
+            const float ksj = ok ? ks[j] : 0.0f;
 #pragma unroll
             for (int u = 0; u < QG; u++) {
                 float sum = 0.0f;
@@ -173,7 +180,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
                     acc = mfma_fp8(qf[u][hs][0], k0, acc);
                     acc = mfma_fp8(qf[u][hs][1], k1, acc);
 #pragma unroll
-                    for (int i = 0; i < 16; i++) sum = fmaf(wr[u][hs][i], fmaxf(acc[i], 0.0f), sum);
+                    for (int blk = 0; blk < 4; blk++) {
+                        // heads 32 hs + 8 blk + 4 g + [0, 4) of accumulator registers 4 blk + [0, 4)
+                        const f32x4 wv = *(const f32x4*)&wsh[wave][u][32 * hs + 8 * blk + 4 * g];
+#pragma unroll
+                        for (int e = 0; e < 4; e++) sum = fmaf(wv[e], fmaxf(acc[4 * blk + e], 0.0f), sum);
+                    }
                 }
                 sum += __shfl_xor(sum, 32, 64);
                 if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = scale * ksj * sum;
