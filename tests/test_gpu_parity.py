@@ -273,6 +273,34 @@ def test_sparse_mla_user_indices_and_edge_cases():
         assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
 
 
+def test_sparse_mla_logits_far_above_the_first_tile():
+    """A selected row whose logit is ~96 nats above every logit of the first tile: the running
+    sum against the first tile's reference overflows the 2^64 margin, so the kernel must take its
+    exact two-pass path.  q = 2 and that row = 2 in every dim (exact in bf16): z = 576*4/24."""
+    rng = np.random.default_rng(12)
+    for H in (16, 128):
+        spec = synth.Spec(f"mla-far-H{H}", ctx=[300, 300], nq=[1, 1], idx_dtype=synth.FP8, topk=100,
+                          mla_heads=H, seed=H + 1)
+        p = synth.build(spec)
+        bits2 = np.uint16(0x4000)                                  # bf16 2.0
+        p.q_mla[:] = bits2
+        big = 1 * p.seq_stride + 250                               # sequence 1, position 250
+        p.latent[big] = bits2
+        dp = to_device(p)
+        k = 100
+        idx = np.full((2, k), -1, np.int32)
+        idx[0, :80] = rng.permutation(240)[:80]                    # no large row: the fast path
+        idx[1, :79] = rng.permutation(240)[:79]
+        idx[1, 79] = 250                                           # the large row, in the third tile
+        it = torch.from_numpy(idx).cuda()
+        out, lse = dsa.dsa_sparse_mla(dp.q_mla, dp.latent, dp.batch, it, spec.softmax_scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle_mla(p, idx)
+        check_mla(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"far H={H}")
+        # the large row dominates: the output is that row's values
+        assert np.abs(out[1].float().cpu().numpy() - 2.0).max() < 1e-2
+
+
 def test_empty_batch_is_a_no_op():
     T = 0
     z = torch.zeros(0, dtype=torch.int32, device="cuda")
