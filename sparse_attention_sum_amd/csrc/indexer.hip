@@ -24,6 +24,11 @@
 namespace dsa {
 namespace {
 
+// max(0, x) as a signed-integer max of the bits: non-negative floats order like their bit patterns,
+// and every negative float (sign bit set) is a negative integer, which becomes +0.  One VALU
+// instruction; fmaxf would add a canonicalising max in IEEE mode.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ---------------------------------------------------------------------------------------------
 // generic path
 
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
     for (int j = 0; j < H; j++) {
         float dot = 0.0f;
         for (int i = 0; i < kIdxDim; i++) dot = fmaf(qs[j * kIdxDim + i], kv[i], dot);
-        total = fmaf(wsh[j], fmaxf(dot, 0.0f), total);
+        total = fmaf(wsh[j], relu_bits(dot), total);
     }
     scores[(int64_t)t * ld + s] = scale * ks * total;
 }
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
                         // heads 32 hs + 8 blk + 4 g + [0, 4) of accumulator registers 4 blk + [0, 4)
                         const f32x4 wv = *(const f32x4*)&wsh[wave][u][32 * hs + 8 * blk + 4 * g];
 #pragma unroll
-                        for (int e = 0; e < 4; e++) sum = fmaf(wv[e], fmaxf(acc[4 * blk + e], 0.0f), sum);
+                        for (int e = 0; e < 4; e++) sum = fmaf(wv[e], relu_bits(acc[4 * blk + e]), sum);
                     }
                 }
                 sum += __shfl_xor(sum, 32, 64);
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
 #pragma unroll
                     for (int ks = 0; ks < 8; ks++) acc = mfma_bf16_32(qf[hs][ks], kf[ks], acc);
 #pragma unroll
-                    for (int i = 0; i < 16; i++) sum = fmaf(wr[hs][i], fmaxf(acc[i], 0.0f), sum);
+                    for (int i = 0; i < 16; i++) sum = fmaf(wr[hs][i], relu_bits(acc[i]), sum);
                 }
                 sum += __shfl_xor(sum, 32, 64);
                 const int s = sb + c;
@@ -313,6 +318,226 @@ __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 prefill path, streamed through LDS by DMA: eight query tokens per workgroup (one per wave,
+// all heads), 64-key tiles fetched with global_load_lds_dwordx4 into a three-deep ring, so the keys
+// pass through no registers and the loop carries almost no per-key address work.
+//
+// Tile layout: DMA instruction r of wave w fills bytes [1024 (2w + r), +1024) of a tile buffer, so
+// lane L writes 16 bytes to key row kr = 4 (2w + r) + L/16, slot L%16.  Slot p of row kr holds the
+// row's 16-byte chunk p ^ (kr & 15): the MFMA-operand reads below (16 lanes reading the same chunk
+// of 16 consecutive rows) then touch 16 distinct 16-byte bank groups.
+// Keys past the longest query of the workgroup, and rows of out-of-range pages, are fetched from an
+// all-zero row, which scores 0 exactly (ReLU(0) = 0).
+//
+// Inside a tile each wave runs 2 * NHS MFMA chains (subtile x head slice, eight MFMAs each); the
+// ReLU-weight epilogue of chain c (32 VALU instructions) is interleaved with the MFMAs of chain c + 1,
+// which keeps the VALU work in the shadow of the matrix unit.
+
+constexpr int kPfWaves = 8;
+constexpr int kPfTile = 64;                              // keys per tile
+constexpr int kPfTileBytes = kPfTile * kIdxDim * 2;      // 16 KiB
+constexpr int kPfTabMax = 4096;                          // tiles per sequence, paged layout (LDS table)
+
+__device__ const uint8_t kZeroKeyRow[kIdxDim * 2] __attribute__((aligned(256))) = {};
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_off(T* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from src into LDS at m0 + 16 * lane.  Written as asm so
+// that the compiler does not track the LDS write: its alias bookkeeping would otherwise drain every
+// DMA in flight (vmcnt(0)) before each read of a tile buffer.  Arrival is awaited explicitly.  The
+// s_nop covers the hazard of m0 written right before a DMA that reads it.
+__device__ __forceinline__ void pf_dma(const uint8_t* src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Waits for this wave's own LDS operations only, then the workgroup barrier (no vmcnt drain: tile
+// DMAs stay in flight across it; their arrival is awaited explicitly).
+__device__ __forceinline__ void pf_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// acc = q_slice . k_subtile^T (32 heads x 32 keys), eight MFMAs; meanwhile the epilogue of the
+// previous chain folds 16 head rows of `prev` into `sum` (w * max(0, x), two VALU per element).
+template <bool EPI>
+__device__ __forceinline__ f32x16 pf_chain(const bf16x8 (&qs)[8], const bf16x8 (&kf)[8], const f32x16& prev,
+                                           const float (&wp)[16], float& sum) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qs[ks], kf[ks], acc, 0, 0, 0);
+        if (EPI) {
+            sum = fmaf(wp[2 * ks], relu_bits(prev[2 * ks]), sum);
+            sum = fmaf(wp[2 * ks + 1], relu_bits(prev[2 * ks + 1]), sum);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the MFMA / VALU interleave as written
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float pf_epilogue(const f32x16& a, const float (&wp)[16], float sum) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) sum = fmaf(wp[i], relu_bits(a[i]), sum);
+    return sum;
+}
+
+template <int NHS>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ q_scale,
+                                const float* __restrict__ w, CacheView kc, BatchView bv, float scale,
+                                float* __restrict__ scores, int64_t ld, int skip_le) {
+    constexpr int H = 32 * NHS;
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_a[kPfTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_b[kPfTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_c[kPfTileBytes];
+    __shared__ int32_t tab[kPfTabMax];      // paged layout: first storage row of each tile, -1 if none
+    __shared__ int nmax_sh;
+
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, c = lane & 31;
+    int qb = bv.cu_q[b], qe = bv.cu_q[b + 1];
+    qb = max(0, min(qb, bv.T));
+    qe = max(qb, min(qe, bv.T));
+    const int tq0 = qb + kPfWaves * (gridDim.x - 1 - blockIdx.x);   // longest groups first
+    if (tq0 >= qe) return;
+    const int t = tq0 + wave;
+    const bool has_q = t < qe;
+    int n = has_q ? min(bv.q_len[t], bv.max_len) : 0;
+    if (n <= skip_le) n = 0;
+    n = max(n, 0);
+    if (threadIdx.x == 0) nmax_sh = 0;
+    __syncthreads();
+    if (lane == 0) atomicMax(&nmax_sh, n);
+    __syncthreads();
+    const int nmax = nmax_sh;
+    if (nmax == 0) return;
+    const int ntiles = (nmax + kPfTile - 1) / kPfTile;
+    const bool paged = kc.page_table != nullptr;
+    if (paged) {
+        for (int j = threadIdx.x; j < ntiles; j += kPfWaves * 64) {
+            const int64_t s0 = (int64_t)j * kPfTile;
+            const int64_t page = kc.page_table[(int64_t)b * kc.pt_stride + s0 / kc.page_size];
+            const int64_t row0 = page * kc.page_size + s0 % kc.page_size;
+            tab[j] = (page >= 0 && row0 < kc.num_rows) ? (int32_t)row0 : -1;
+        }
+    }
+
+    // operands of this wave's query: head 32 hs + c, dims 64 g + 8 ks .. +8
+    bf16x8 qf[NHS][8];
+    float wr[NHS][16];
+    const int tq = has_q ? t : tq0;
+#pragma unroll
+    for (int hs = 0; hs < NHS; hs++) {
+        const uint16_t* src = q + ((int64_t)tq * H + 32 * hs + c) * kIdxDim + 64 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) qf[hs][ks] = *(const bf16x8*)(src + 8 * ks);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int r = 32 * hs + 8 * (i / 4) + 4 * g + (i % 4);
+            const float sc = q_scale ? q_scale[(int64_t)tq * H + r] : 1.0f;
+            wr[hs][i] = w[(int64_t)tq * H + r] * sc;
+        }
+    }
+    if (paged) __syncthreads();   // the page table above
+    __builtin_amdgcn_s_waitcnt(0);   // operands in registers before any tile DMA is counted
+
+    // DMA of tile j into buf: two instructions per wave, 4 key rows each
+    const int kr_base = 8 * wave + (lane >> 4);
+    auto issue = [&](int j, uint8_t* buf) {
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const int kr = kr_base + 4 * r;
+            const int64_t s = (int64_t)j * kPfTile + kr;
+            const uint8_t* src = kZeroKeyRow;
+            if (s < nmax) {
+                int64_t row;
+                if (paged) {
+                    const int r0 = tab[j];
+                    row = (r0 >= 0 && (int64_t)r0 + kr < kc.num_rows) ? (int64_t)r0 + kr : -1;
+                } else {
+                    row = (int64_t)b * kc.seq_stride + s;
+                }
+                if (row >= 0) src = (const uint8_t*)kc.data + row * (kIdxDim * 2);
+            }
+            src += 16 * ((lane & 15) ^ (kr & 15));
+            pf_dma(src, lds_off(buf) + (2 * wave + r) * 1024);
+        }
+    };
+
+    // MFMA-operand read offsets: lane (g, c) takes chunk 8 g + ks of row c of a 32-key subtile
+    uint32_t roff[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) roff[ks] = 256 * c + 16 * ((8 * g + ks) ^ (c & 15));
+
+    float pend[2] = {0.0f, 0.0f};
+    int pend_s0 = -1;
+    float* srow = scores + (int64_t)t * ld;
+    auto flush = [&]() {
+        if (pend_s0 >= 0 && g == 0) {
+#pragma unroll
+            for (int sub = 0; sub < 2; sub++) {
+                const int s = pend_s0 + 32 * sub + c;
+                if (s < n) srow[s] = pend[sub];
+            }
+        }
+        pend_s0 = -1;
+    };
+
+    auto compute = [&](const uint8_t* buf, int j) {
+        const int s0 = j * kPfTile;
+        if (s0 >= n) return;
+        const bool two = s0 + 32 < n;
+        bf16x8 kf0[8], kf1[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) kf0[ks] = *(const bf16x8*)(buf + roff[ks]);
+        if (two) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ks++) kf1[ks] = *(const bf16x8*)(buf + 8192 + roff[ks]);
+        }
+        float sum0 = 0.0f, sum1 = 0.0f;
+        const f32x16 none = {};
+        f32x16 x = pf_chain<false>(qf[0], kf0, none, wr[0], sum0);
+        if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf0, x, wr[0], sum0);
+        if (two) {
+            x = pf_chain<true>(qf[0], kf1, x, wr[NHS - 1], sum0);
+            if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf1, x, wr[0], sum1);
+            sum1 = pf_epilogue(x, wr[NHS - 1], sum1);
+        } else {
+            sum0 = pf_epilogue(x, wr[NHS - 1], sum0);
+        }
+        // the two 32-lane halves hold the two 16-head halves of every 32-head slice
+        const auto h0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum0), __float_as_uint(sum0), false, false);
+        const auto h1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum1), __float_as_uint(sum1), false, false);
+        pend[0] = scale * (sum0 + __uint_as_float(h0[1]));
+        pend[1] = scale * (sum1 + __uint_as_float(h1[1]));
+        pend_s0 = s0;
+    };
+
+    // tile j sits in buffer j % 3; the DMA of tile j + 2 goes to the buffer tile j - 1 used
+    auto step = [&](int j, const uint8_t* cur, uint8_t* ahead) {
+        if (j + 1 < ntiles)
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");   // this wave's part of tile j is in LDS
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        pf_barrier();                                           // everyone's part; tile j - 1 is free
+        if (j + 2 < ntiles) issue(j + 2, ahead);
+        flush();
+        compute(cur, j);
+    };
+
+    issue(0, tile_a);
+    if (ntiles > 1) issue(1, tile_b);
+    for (int j = 0; j < ntiles; j += 3) {
+        step(j, tile_a, tile_c);
+        if (j + 1 < ntiles) step(j + 1, tile_b, tile_a);
+        if (j + 2 < ntiles) step(j + 2, tile_c, tile_b);
+    }
+    flush();
 }
 
 }  // namespace
@@ -337,6 +562,18 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
             else
                 indexer_fp8_decode_kernel<2, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
         }
+        return hipGetLastError();
+    }
+    const bool stream_layout = kc.page_table == nullptr ||
+                               (kc.page_size % kPfTile == 0 && (int64_t)bv.max_len <= (int64_t)kPfTabMax * kPfTile);
+    if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2) && kc.scale == nullptr && stream_layout) {
+        dim3 grid((bv.max_q + kPfWaves - 1) / kPfWaves, bv.B);
+        if (nhs == 1)
+            indexer_bf16_stream_kernel<1><<<grid, kPfWaves * 64, 0, st>>>(
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+        else
+            indexer_bf16_stream_kernel<2><<<grid, kPfWaves * 64, 0, st>>>(
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
         return hipGetLastError();
     }
     if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2)) {

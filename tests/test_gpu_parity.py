@@ -159,13 +159,19 @@ SMALL = [
     ("mtp-fp8-h32", [70, 129, 3000], [2, 2, 2], 32, synth.FP8, 64, 64, False),
     ("decode-bf16-contig", [500, 1025], [1, 1], 64, synth.BF16, 128, 48, False),
     ("decode-f32-generic", [600, 90], [3, 1], 8, synth.F32, 50, 8, True),
+    # bf16 prefill over several sequences, queries at the end of a longer context, 64-token pages
+    ("prefill-bf16-3seq-paged", [200, 777, 64], [200, 300, 64], 64, synth.BF16, 128, 16, True),
+    # 16-token pages: the bf16 kernel for any cache layout
+    ("prefill-bf16-page16", [333, 130], [100, 130], 64, synth.BF16, 64, 16, True, 16),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_workloads_all_rows(case):
-    name, ctx, nq, hi, dt, k, h, paged = case
-    spec = synth.Spec(name, ctx=ctx, nq=nq, idx_heads=hi, idx_dtype=dt, topk=k, mla_heads=h, paged=paged, seed=11)
+    name, ctx, nq, hi, dt, k, h, paged = case[:8]
+    page_size = case[8] if len(case) > 8 else synth.PAGE
+    spec = synth.Spec(name, ctx=ctx, nq=nq, idx_heads=hi, idx_dtype=dt, topk=k, mla_heads=h, paged=paged,
+                      page_size=page_size, seed=11)
     dp = device_problem(spec)
     T = spec.T
     check_problem(dp, range(T), range(T), range(T), name)
@@ -197,6 +203,38 @@ def test_paged_equals_contiguous_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dt,nq", [(synth.BF16, [300, 1]), (synth.FP8, [1, 1]), (synth.FP8, [300, 1])],
+                         ids=["bf16-prefill", "fp8-decode", "fp8-generic"])
+def test_indexer_out_of_range_pages_read_as_zero_rows(dt, nq):
+    """Page numbers outside [0, num_pages) read as all-zero key rows: those tokens score exactly 0
+    (ReLU(0) = 0) and every other score is unchanged, bit for bit."""
+    spec = synth.Spec(f"badpage-{dt}-{nq[0]}", ctx=[700, 300], nq=nq, idx_heads=64, idx_dtype=dt, topk=64,
+                      paged=True, seed=13)
+    p = synth.build(spec)
+    dp = to_device(p)
+    b = dp.batch
+    ld = dsa.score_ld(b)
+    s1 = dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, b, scale=spec.idx_scale, ld=ld)
+    pt = p.page_table.copy()
+    num_pages = p.k_idx.shape[0] // synth.PAGE
+    pt[0, 2] = -1                      # tokens 128..191 of sequence 0
+    pt[0, 5] = num_pages               # tokens 320..383
+    pt[1, 1] = -7                      # tokens 64..127 of sequence 1
+    kc = dsa.Cache(dp.k_cache.data, dp.k_cache.scale, page_table=torch.from_numpy(pt).cuda(), page_size=synth.PAGE)
+    s2 = dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, kc, b, scale=spec.idx_scale, ld=ld)
+    torch.cuda.synchronize()
+    s1, s2 = s1.cpu().numpy(), s2.cpu().numpy()
+    bad = {0: [(128, 192), (320, 384)], 1: [(64, 128)]}
+    for t in range(spec.T):
+        n = int(p.q_len[t])
+        seq = int(p.q_seq[t])
+        mask = np.zeros(n, bool)
+        for lo, hi in bad[seq]:
+            mask[lo:min(hi, n)] = True
+        assert np.all(s2[t, :n][mask] == 0.0), f"row {t}: a token of a bad page scored nonzero"
+        assert np.array_equal(s2[t, :n][~mask], s1[t, :n][~mask]), f"row {t}: other scores changed"
 
 
 def test_deterministic_repeat():
