@@ -44,6 +44,7 @@ constexpr int kRowChunks = kDqk * 2 / 16;       // 72 16-byte chunks per latent 
 constexpr int kRowSlots = kRowChunks + 1;       // LDS row = 72 chunks + 1 pad chunk (bank spread)
 constexpr int kRowB = kRowSlots * 16;           // 1168 bytes
 constexpr int kTileSlots = kTile * kRowSlots;   // 2336 16-byte LDS slots per tile
+constexpr int kTileB = kTileSlots * 16;
 constexpr int kLoadsPerWave = (kTileSlots + kMlaThreads - 1) / kMlaThreads;
 constexpr int kMaxList = 2048;                  // index slots per split
 constexpr int kAhead = 2;                       // logit operand reads in flight
@@ -83,9 +84,9 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
     // Three distinct LDS tiles: with fixed roles per (unrolled) iteration the compiler can tell that
     // reads of one tile do not depend on the in-flight global->LDS loads into the others.
-    __shared__ __attribute__((aligned(16))) uint8_t tile_a[kTile * kRowB];
-    __shared__ __attribute__((aligned(16))) uint8_t tile_b[kTile * kRowB];
-    __shared__ __attribute__((aligned(16))) uint8_t tile_c[kTile * kRowB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_a[kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_b[kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_c[kTileB];
     __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][4][64];   // partial-logit exchange
     __shared__ int32_t rows[kMaxList];
     __shared__ int wcount[kMlaWaves];
@@ -108,33 +109,55 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     if (lane == 0) xflag[wave] = 0;
 
-    // query half-block (loads issued first, so their latency overlaps the index compaction):
-    // lane (g, c32) holds head 32*hg + c32, dims 288*half + 16*kk + 8*g + [0, 8)
     const int hq = kHeadsPerGroup * hg + c32;
     const bool wave_on = kHeadsPerGroup * hg < H;
+
+    // Memory order of the prologue: the first pass of index reads, then the query half-block, then
+    // (after the compaction) the first two tile gathers.  The compaction synchronises through LDS
+    // only, so the query loads -- 18 per lane, each spanning 32 head rows -- stay in flight while
+    // it runs.
+    // The first 512 index entries go straight into LDS (tile_c is unused until the loop) with a
+    // global_load_lds_dword issued in asm; the asm also takes the query pointer, so the compiler
+    // keeps the query loads after it, and exactly kQf of them follow -- the explicit vmcnt below
+    // relies on that count.  Every load here is unconditional, from a clamped in-range address,
+    // with the value selected afterwards.
+    constexpr int kQf = kQkHalf / 16;
+    const uint16_t* qrow = q + ((int64_t)t * H + (kHeadsPerGroup * hg + c32 < H ? hq : 0)) * kDqk + kQkHalf * half + 8 * g;
+    {
+        const int32_t* src = idx + (int64_t)t * k + min(j0 + tid, k - 1);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                     ::"v"(src), "{m0}"(lds_addr(tile_c) + 256 * __builtin_amdgcn_readfirstlane(wave)), "v"(qrow)
+                     : "memory");
+    }
+    // query half-block: lane (g, c32) holds head 32*hg + c32, dims 288*half + 16*kk + 8*g + [0, 8).
     // The last of the 18 fragments is parked in LDS (read back once per tile): with all 18 in
     // VGPRs the loop needs one register more than the 256 it has at two waves per SIMD, and a
     // scratch reload would wait for the tile loads in flight.
-    constexpr int kQf = kQkHalf / 16;
     bf16x8 qf[kQf - 1];
     const bf16x8 zero8 = {};
     const bool q_on = wave_on && hq < H;
-    const uint16_t* qrow = q + ((int64_t)t * H + hq) * kDqk + kQkHalf * half + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < kQf - 1; kk++) qf[kk] = q_on ? *(const bf16x8*)(qrow + 16 * kk) : zero8;
-    qlast[wave][lane] = q_on ? *(const bf16x8*)(qrow + 16 * (kQf - 1)) : zero8;
-    const uint32_t qlast_addr = lds_addr(&qlast[wave][lane]);
+    for (int kk = 0; kk < kQf - 1; kk++) {
+        const bf16x8 v = *(const bf16x8*)(qrow + 16 * kk);
+        qf[kk] = q_on ? v : zero8;
+    }
+    const bf16x8 q_last_raw = *(const bf16x8*)(qrow + 16 * (kQf - 1));
+    const bf16x8 q_last = q_on ? q_last_raw : zero8;
+    // the index DMA has landed once at most the kQf query loads issued after it are outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kQf), "v"(qrow) : "memory");
+    const int raw_first = ((const int32_t*)tile_c)[tid];
+    const int s_first = j0 + tid < j1 ? raw_first : -1;
 
     // 0. compact the valid selected positions of this split into storage rows
     int cnt = 0;
     for (int base = j0; base < j1; base += kMlaThreads) {
         const int slot = base + tid;
-        const int s = slot < j1 ? idx[(int64_t)t * k + slot] : -1;
+        const int s = base == j0 ? s_first : slot < j1 ? idx[(int64_t)t * k + slot] : -1;
         const int64_t row = (s >= 0 && s < n) ? cache_row(lat, b, s) : -1;
         const bool valid = row >= 0;
         const uint64_t bal = __ballot(valid);
         if (lane == 0) wcount[wave] = __popcll(bal);
-        __syncthreads();
+        lds_barrier();
         int off = cnt, tot = 0;
         for (int w = 0; w < kMlaWaves; w++) {
             if (w < wave) off += wcount[w];
@@ -142,14 +165,14 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         }
         if (valid) rows[off + __popcll(bal & lt_mask)] = (int32_t)row;
         cnt += tot;
-        __syncthreads();
+        lds_barrier();
     }
 
     const int ntiles = (cnt + kTile - 1) / kTile;
     // 1. gather a tile straight into LDS: wave instruction r of wave w fills LDS slots
-    //    [64 (8 r + w), +64); slot p holds chunk p % 73 of tile row p / 73 (the 73rd slot of a row
-    //    is padding and is not loaded).  Rows past the end of the list repeat the last selected
-    //    row, so every LDS value stays finite; their logits are masked to -inf.
+    //    [64 (8 r + w), +64) of the layout above (padding slots are not loaded).  Rows past the end
+    //    of the list repeat the last selected row, so every LDS value stays finite; their logits
+    //    are masked to -inf.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int my_loads = (kTileSlots - wave_u * 64 + kMlaThreads - 1) / kMlaThreads;   // instructions per tile
     auto load_tile = [&](int tile, uint8_t* tb) {
@@ -160,8 +183,6 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int rbase = tile * kTile, last = cnt - 1;
 #pragma unroll
         for (int r = 0; r < kLoadsPerWave; r++) {
-            // slot p = p0 + lane: row p / 73, chunk p % 73, from the wave-uniform split of p0 plus
-            // at most one wrap (lane < 64 < 73)
             const int p0 = (r * kMlaWaves + wave_u) * 64;
             const int rr0 = p0 / kRowSlots, cc0 = p0 - rr0 * kRowSlots;
             const int c = cc0 + lane_o;
@@ -191,6 +212,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     };
     if (ntiles > 0) load_tile(0, tile_a);
     if (ntiles > 1) load_tile(1, tile_b);
+    qlast[wave][lane] = q_last;   // waits for the query loads only; the gathers stay in flight
+    const uint32_t qlast_addr = lds_addr(&qlast[wave][lane]);
 
     f32x16 oacc[kVHalf / 32];
 #pragma unroll
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // dims 16*(G%2) of each 32-dim block; lane jj of the group points at row 4g + jj/4 (+16m + 8h
     // per step) and dims 4*(jj%4).
     const int G = lane >> 4, jj = lane & 15;
-    const int v_off = (4 * g + (jj >> 2)) * kRowB + 32 * (G & 1) + 8 * (jj & 3) + 2 * kVHalf * half;
+    const int v_off = kRowB * (4 * g + (jj >> 2)) + 32 * (G & 1) + 8 * (jj & 3) + 2 * kVHalf * half;
 
     // 2. partial logits over this wave's half of the query dims; register i holds key
     //    8*(i/4) + 4*g + i%4 of the tile for head c32
@@ -211,6 +234,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // read back for the tile loads in flight
         bf16x8 ql;
         asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(ql) : "v"(qlast_addr) : "memory");
+        // the lane number passes through an empty asm: the row offset is recomputed here (a few
+        // VALU per tile) rather than held in a register across the loop
         const uint8_t* rp = tb + c32 * kRowB + 16 * g + 2 * kQkHalf * half;
         bf16x8 kb[kAhead];
 #pragma unroll
