@@ -29,7 +29,8 @@ constexpr int kCap = 32768;          // keys cached in LDS (128 KiB)
 constexpr int kCandCap = kCap / 2;   // candidates of a long row: keys + positions (128 KiB)
 constexpr int kLdsWords = kCap;      // dynamic LDS words of a launch whose rows may exceed kCap
 
-constexpr int kUnroll = 16;    // 16-byte loads in flight per thread
+constexpr int kUnroll = 8;     // 16-byte loads in flight per thread, rows cached in LDS
+constexpr int kUnrollLong = 16; // the same for rows read from global memory on every pass
 constexpr int kDigitBits = 11; // radix digit width
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 2;
@@ -43,37 +44,38 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);       // monotone in the real value
 }
 
-// f(i, key) for every position i < n of a score row in global memory (each i once, in no set order).
-template <typename F>
-__device__ __forceinline__ void for_each_raw(const float* __restrict__ srow, int n, bool vec, F&& f) {
+// f4(i, keys) for every aligned group of four positions i .. i+3 < n of a score row in global memory
+// (16-byte loads, kUnroll of them in flight per thread), then f1(i, key) for the tail positions;
+// each position once, in no set order.  Rows that are not 16-byte aligned use f1 throughout.
+template <int U, typename F4, typename F1>
+__device__ __forceinline__ void for_each_raw4(const float* __restrict__ srow, int n, bool vec, F4&& f4, F1&& f1) {
     const int tid = threadIdx.x;
-    if (!vec) {
-        for (int i = tid; i < n; i += kTkBlock) f(i, order_key(srow[i]));
-        return;
-    }
-    for (int base = 0; base < n; base += kTkBlock * 4 * kUnroll) {
-        float4 v[kUnroll];
+    int done = 0;
+    if (vec) {
+        const int n4 = n >> 2;
+        const float4* s4 = (const float4*)srow;
+        for (int base = 0; base < n4; base += U * kTkBlock) {
+            float4 v[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int i = base + 4 * (u * kTkBlock + tid);
-            if (i + 3 < n) {
-                v[u] = *(const float4*)(srow + i);
-            } else {
-                v[u].x = i < n ? srow[i] : 0.0f;
-                v[u].y = i + 1 < n ? srow[i + 1] : 0.0f;
-                v[u].z = i + 2 < n ? srow[i + 2] : 0.0f;
-                v[u].w = 0.0f;
+            for (int u = 0; u < U; u++) {
+                const int j = base + u * kTkBlock + tid;
+                if (j < n4) v[u] = s4[j];
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = base + u * kTkBlock + tid;
+                if (j < n4) f4(4 * j, uint4{order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)});
             }
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int i = base + 4 * (u * kTkBlock + tid);
-            if (i < n) f(i, order_key(v[u].x));
-            if (i + 1 < n) f(i + 1, order_key(v[u].y));
-            if (i + 2 < n) f(i + 2, order_key(v[u].z));
-            if (i + 3 < n) f(i + 3, order_key(v[u].w));
-        }
+        done = 4 * n4;
     }
+    for (int i = done + tid; i < n; i += kTkBlock) f1(i, order_key(srow[i]));
+}
+
+template <typename F>
+__device__ __forceinline__ void for_each_raw(const float* __restrict__ srow, int n, bool vec, F&& f) {
+    for_each_raw4<kUnrollLong>(srow, n, vec,
+                               [&](int i, const uint4& kk) { f(i, kk.x); f(i + 1, kk.y); f(i + 2, kk.z); f(i + 3, kk.w); }, f);
 }
 
 // The same over keys held in LDS (16-byte reads; the array is 16-byte aligned).
@@ -118,12 +120,40 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     return (uint32_t)x;
 }
 
+// Wave-wide min / max with the same DPP pattern as wave_incl_scan: after the four row shifts the
+// last lane of each 16-lane row holds its row's result, the two broadcasts carry it up, and lane
+// 63 ends with the wave's result, which readlane hands to every lane.  Out-of-range sources read
+// the identity (`old`).
+__device__ __forceinline__ uint32_t wave_reduce_max(uint32_t v) {
+    int x = (int)v;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ uint32_t wave_reduce_min(uint32_t v) {
+    int x = (int)v;
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x111, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x112, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x114, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x118, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
 // Ordered compaction: every working-set entry with (key & mask) > thr, plus the first need_eq
-// entries with (key & mask) == thr, in entry order.  Wave w owns entries [beg, end); an iteration
-// covers 256 entries as four groups of 64 consecutive ones (one per lane), so each group's slots
-// come from a ballot and a popcount, and the four loads of an iteration are in flight together.
-template <typename KeyAt, typename PosAt>
-__device__ __forceinline__ void compact(KeyAt&& key_at, PosAt&& pos_at, int nw, uint32_t mask, uint32_t thr,
+// entries with (key & mask) == thr, in entry order.  Wave w owns entries [beg, end) (beg a multiple
+// of 256); a step covers 256 entries, lane L holding entries base + 4L .. +3 (one 16-byte read).
+// The first pass counts the wave's entries above / equal to the threshold; in the second, an
+// inclusive DPP scan over the lanes' packed (above, equal) counts gives every lane the output slot
+// of its first take -- equal entries are taken in entry order while the running count of earlier
+// equal entries is below need_eq.
+template <typename Key4, typename Pos4>
+__device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32_t mask, uint32_t thr,
                                         uint32_t need_eq, int k, int32_t* __restrict__ orow,
                                         uint32_t (&wcnt)[2][kTkWaves]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -131,46 +161,59 @@ __device__ __forceinline__ void compact(KeyAt&& key_at, PosAt&& pos_at, int nw, 
     const int beg = min(nw, wave * seg), end = min(nw, beg + seg);
     uint32_t cgt = 0, ceq = 0;
     for (int base = beg; base < end; base += 256) {
-        uint32_t kk[4];
+        const int i0 = base + 4 * lane;
+        const uint4 kk = key4(i0, end);
+        const uint32_t v[4] = {kk.x & mask, kk.y & mask, kk.z & mask, kk.w & mask};
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int i = base + 64 * j + lane;
-            kk[j] = i < end ? key_at(i) & mask : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int i = base + 64 * j + lane;
-            cgt += __popcll(__ballot(i < end && kk[j] > thr));
-            ceq += __popcll(__ballot(i < end && kk[j] == thr));
+            const bool ok = i0 + j < end;
+            cgt += (ok && v[j] > thr) ? 1u : 0u;
+            ceq += (ok && v[j] == thr) ? 1u : 0u;
         }
     }
+    cgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cgt), 63);
+    ceq = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ceq), 63);
     if (lane == 0) { wcnt[0][wave] = cgt; wcnt[1][wave] = ceq; }
     __syncthreads();
     uint32_t gt_before = 0, eq_before = 0;
     for (int w = 0; w < wave; w++) { gt_before += wcnt[0][w]; eq_before += wcnt[1][w]; }
     uint32_t pos = gt_before + min(eq_before, need_eq);   // output slot of this wave's next take
     uint32_t eq_rank = eq_before;                          // equal entries before this wave's next
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = beg; base < end; base += 256) {
-        uint32_t kk[4];
+        const int i0 = base + 4 * lane;
+        const uint4 kk = key4(i0, end);
+        const int4 pp = pos4(i0);
+        const uint32_t v[4] = {kk.x & mask, kk.y & mask, kk.z & mask, kk.w & mask};
+        const int p[4] = {pp.x, pp.y, pp.z, pp.w};
+        uint32_t g = 0, e = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int i = base + 64 * j + lane;
-            kk[j] = i < end ? key_at(i) & mask : 0u;
+            const bool ok = i0 + j < end;
+            g += (ok && v[j] > thr) ? 1u : 0u;
+            e += (ok && v[j] == thr) ? 1u : 0u;
         }
+        const uint32_t own = g | (e << 16);                 // at most 256 of each per step
+        const uint32_t incl = wave_incl_scan(own);
+        const uint32_t excl = incl - own;
+        const uint32_t quota = need_eq > eq_rank ? need_eq - eq_rank : 0u;   // equal entries still to take
+        uint32_t eq_seen = excl >> 16;
+        uint32_t at = pos + (excl & 0xffffu) + min(eq_seen, quota);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int i = base + 64 * j + lane;
-            const bool gt = i < end && kk[j] > thr;
-            const bool eq = i < end && kk[j] == thr;
-            const uint64_t beq = __ballot(eq);
-            const bool take = gt || (eq && eq_rank + (uint32_t)__popcll(beq & lt_mask) < need_eq);
-            const uint64_t btake = __ballot(take);
-            const uint32_t at = pos + (uint32_t)__popcll(btake & lt_mask);
-            if (take && at < (uint32_t)k) orow[at] = pos_at(i);
-            pos += __popcll(btake);
-            eq_rank += __popcll(beq);
+            const bool ok = i0 + j < end;
+            bool take = ok && v[j] > thr;
+            if (ok && v[j] == thr) {
+                take = eq_seen < quota;
+                eq_seen++;
+            }
+            if (take) {
+                if (at < (uint32_t)k) orow[at] = p[j];
+                at++;
+            }
         }
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        pos += (tot & 0xffffu) + min(tot >> 16, quota);
+        eq_rank += tot >> 16;
     }
 }
 
@@ -201,16 +244,33 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     // kUnroll of them in flight per thread, when it is 16-byte aligned
     const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    {
-        const bool cache = mode == kModeCached;
-        for_each_raw(srow, n, vec, [&](int i, uint32_t kk) {
-            if (cache) keys[i] = kk;
-            lo = min(lo, kk);
-            hi = max(hi, kk);
-        });
+    if (mode == kModeCached) {
+        for_each_raw4<kUnroll>(
+            srow, n, vec,
+            [&](int i, const uint4& kk) {
+                *(uint4*)(keys + i) = kk;
+                lo = min(lo, min(min(kk.x, kk.y), min(kk.z, kk.w)));
+                hi = max(hi, max(max(kk.x, kk.y), max(kk.z, kk.w)));
+            },
+            [&](int i, uint32_t kk) {
+                keys[i] = kk;
+                lo = min(lo, kk);
+                hi = max(hi, kk);
+            });
+    } else {
+        for_each_raw4<kUnrollLong>(
+            srow, n, vec,
+            [&](int, const uint4& kk) {
+                lo = min(lo, min(min(kk.x, kk.y), min(kk.z, kk.w)));
+                hi = max(hi, max(max(kk.x, kk.y), max(kk.z, kk.w)));
+            },
+            [&](int, uint32_t kk) {
+                lo = min(lo, kk);
+                hi = max(hi, kk);
+            });
     }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
+    lo = wave_reduce_min(lo);
+    hi = wave_reduce_max(hi);
     if (lane == 0) { red[0][wave] = lo; red[1][wave] = hi; }
     __syncthreads();
     lo = red[0][0];
@@ -218,8 +278,18 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     for (int w = 1; w < kTkWaves; w++) { lo = min(lo, red[0][w]); hi = max(hi, red[1][w]); }
     __syncthreads();
 
-    auto key_at = [&](int i) -> uint32_t { return mode == kModeGlobal ? order_key(srow[i]) : lds[i]; };
-    auto pos_at = [&](int i) -> int { return mode == kModeCand ? cpos[i] : i; };
+    // entries i .. i+3 of the working set (positions at or past `end` are never used)
+    auto key4 = [&](int i, int end) -> uint4 {
+        if (mode != kModeGlobal) return *(const uint4*)(lds + i);
+        if (vec && i + 3 < end)
+            return uint4{order_key(srow[i]), order_key(srow[i + 1]), order_key(srow[i + 2]), order_key(srow[i + 3])};
+        return uint4{i < end ? order_key(srow[i]) : 0u, i + 1 < end ? order_key(srow[i + 1]) : 0u,
+                     i + 2 < end ? order_key(srow[i + 2]) : 0u, 0u};
+    };
+    auto pos4 = [&](int i) -> int4 {
+        if (mode == kModeCand) return *(const int4*)(cpos + i);
+        return int4{i, i + 1, i + 2, i + 3};
+    };
 
     uint32_t prefix = lo;            // bits resolved so far (under `mask`)
     uint32_t mask = 0xffffffffu;
@@ -339,7 +409,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     // exit, where the bin holds exactly `remaining` keys).  (All keys equal: the first k.)
     const uint32_t thr = prefix, need_eq = remaining;
 
-    compact(key_at, pos_at, nw, mask, thr, need_eq, k, orow, wcnt);
+    compact(key4, pos4, nw, mask, thr, need_eq, k, orow, wcnt);
 }
 
 }  // namespace
