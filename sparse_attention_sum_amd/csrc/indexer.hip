@@ -130,11 +130,47 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
         // storage rows of the wave's subtiles: lane (g, c) reads key key0 + 32*sub + c
         uint32_t rowv[kSub];
         uint32_t okm = 0;                  // bit sub: the key's page is valid
+        if (kc.page_table == nullptr) {
 #pragma unroll
-        for (int sub = 0; sub < kSub; sub++) {
-            const int64_t row = cache_row(kc, b, min<int64_t>(key0 + 32 * sub + c, nmax - 1));
-            rowv[sub] = row >= 0 ? (uint32_t)row : 0u;
-            okm |= row >= 0 ? (1u << sub) : 0u;
+            for (int sub = 0; sub < kSub; sub++) {
+                const int64_t s = key0 + 32 * sub + c < nmax ? key0 + 32 * sub + c : (int64_t)nmax - 1;
+                rowv[sub] = (uint32_t)((int64_t)b * kc.seq_stride + s);
+                okm |= 1u << sub;
+            }
+        } else {
+            // all page-table reads first, then the row arithmetic: the reads are in flight together
+            // (positions and page numbers fit 32 bits: one 32-bit division per key, its quotient reused)
+            int32_t pg[kSub], off[kSub];
+            const int32_t* pt = kc.page_table + (int64_t)b * kc.pt_stride;
+            const int ps = kc.page_size;
+#pragma unroll
+            for (int sub = 0; sub < kSub; sub++) {
+                const int s = min((int)key0 + 32 * sub + c, nmax - 1);
+                const int pi = s / ps;
+                off[sub] = s - pi * ps;
+                pg[sub] = pt[pi];
+            }
+#pragma unroll
+            for (int sub = 0; sub < kSub; sub++) {
+                const int64_t row = (int64_t)pg[sub] * ps + off[sub];
+                const bool ok = pg[sub] >= 0 && row < kc.num_rows;
+                rowv[sub] = ok ? (uint32_t)row : 0u;
+                okm |= ok ? (1u << sub) : 0u;
+            }
+        }
+        // Memory order: this pass's head weights first (a lane loads at most H/64 of them), then the
+        // first PF key subtiles, then the query block; the weights go to LDS after all of that is
+        // issued, so that store waits for the weight loads only, not for the key stream behind them.
+        float wv_raw[QG][(H + 63) / 64], sv_raw[QG][(H + 63) / 64];
+#pragma unroll
+        for (int u = 0; u < QG; u++) {
+            const int t = t0 + (u < nq ? u : 0);
+#pragma unroll
+            for (int j = 0; j < (H + 63) / 64; j++) {
+                const int r = min(lane + 64 * j, H - 1);
+                wv_raw[u][j] = w[(int64_t)t * H + r];
+                sv_raw[u][j] = q_scale ? q_scale[(int64_t)t * H + r] : 1.0f;
+            }
         }
         i32x8 kf[PF][2];
         float ks[PF];
@@ -147,14 +183,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
 #pragma unroll
         for (int j = 0; j < PF; j++) load_keys(j, j);
 
-        // this pass's weights into the wave's own LDS area (no other wave reads it)
-#pragma unroll
-        for (int u = 0; u < QG; u++)
-            for (int r = lane; r < H; r += 64) {
-                const int t = t0 + (u < nq ? u : 0);
-                const float sc = q_scale ? q_scale[(int64_t)t * H + r] : 1.0f;
-                wsh[wave][u][r] = u < nq ? w[(int64_t)t * H + r] * sc : 0.0f;
-            }
         i32x8 qf[QG][NHS][2];
 #pragma unroll
         for (int u = 0; u < QG; u++) {
@@ -166,6 +194,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
                 qf[u][hs][1] = *(const i32x8*)(src + 32);
             }
         }
+        // this pass's weights into the wave's own LDS area (no other wave reads it)
+#pragma unroll
+        for (int u = 0; u < QG; u++)
+#pragma unroll
+            for (int j = 0; j < (H + 63) / 64; j++) {
+                const int r = lane + 64 * j;
+                if (r < H) wsh[wave][u][r] = u < nq ? wv_raw[u][j] * sv_raw[u][j] : 0.0f;
+            }
 
 #pragma unroll
         for (int sub = 0; sub < kSub; sub++) {
