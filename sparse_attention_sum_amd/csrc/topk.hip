@@ -55,16 +55,26 @@ __device__ __forceinline__ void for_each_raw4(const float* __restrict__ srow, in
         const int n4 = n >> 2;
         const float4* s4 = (const float4*)srow;
         for (int base = 0; base < n4; base += U * kTkBlock) {
+            // every load is issued (clamped to the last vector) so that they all stay in flight
+            // together; positions past the end are skipped below
             float4 v[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int j = base + u * kTkBlock + tid;
-                if (j < n4) v[u] = s4[j];
+                v[u] = s4[j < n4 ? j : n4 - 1];
             }
+            if (base + U * kTkBlock <= n4) {  // uniform: a whole batch, no guards
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int j = base + u * kTkBlock + tid;
-                if (j < n4) f4(4 * j, uint4{order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)});
+                for (int u = 0; u < U; u++) {
+                    const int j = base + u * kTkBlock + tid;
+                    f4(4 * j, uint4{order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)});
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const int j = base + u * kTkBlock + tid;
+                    if (j < n4) f4(4 * j, uint4{order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w)});
+                }
             }
         }
         done = 4 * n4;
