@@ -176,14 +176,15 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int my_loads = (kTileSlots - wave_u * 64 + kMlaThreads - 1) / kMlaThreads;   // instructions per tile
     auto load_tile = [&](int tile, uint8_t* tb) {
-        // the lane number passes through an empty asm so that the per-lane slot arithmetic below is
+        // the lane and wave numbers pass through an empty asm so that the slot arithmetic below is
         // redone at each call instead of being hoisted into registers that stay live all loop long
-        int lane_o = lane;
-        asm volatile("" : "+v"(lane_o));
+        // (held, the wave-uniform offsets alone took some twenty scalar registers)
+        int lane_o = lane, wave_o = wave_u;
+        asm volatile("" : "+v"(lane_o), "+s"(wave_o));
         const int rbase = tile * kTile, last = cnt - 1;
 #pragma unroll
         for (int r = 0; r < kLoadsPerWave; r++) {
-            const int p0 = (r * kMlaWaves + wave_u) * 64;
+            const int p0 = (r * kMlaWaves + wave_o) * 64;
             const int rr0 = p0 / kRowSlots, cc0 = p0 - rr0 * kRowSlots;
             const int c = cc0 + lane_o;
             const bool wrap = c >= kRowSlots;
@@ -360,11 +361,15 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     //    the workgroup redoes the split in two passes with a fresh accumulator (exact max first).
     //    Every wave takes part in the exchange barrier, also waves without heads.
     bool over = false;
-    auto fast_tile = [&](int tile, const uint8_t* tb) {
+    auto fast_tile = [&](int tile, const uint8_t* tb, uint8_t* nb) {
         // every wave runs the QK step (a wave without heads holds a zero query block); the fences
-        // keep the scheduler from stretching register lifetimes across it
+        // keep the scheduler from stretching register lifetimes across it.  Tile i + 2 is gathered
+        // into the buffer that tile i - 1 freed once this wave's QK step is issued: waves reach this
+        // point at different times, so the workgroup's gathers do not all queue at the barrier.
         __builtin_amdgcn_sched_barrier(0);
         f32x16 z = qk_tile(tb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tile + 2 < ntiles) load_tile(tile + 2, nb);
         __builtin_amdgcn_sched_barrier(0);
         const float mt = logits(tile, z);
         if (!wave_on) return;
@@ -376,19 +381,17 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     wait_ahead(true, ntiles > 1);
     lds_barrier();
     for (int tile = 0; tile < ntiles; tile += 3) {
-        // tile i is consumed while tiles i+1 (issued earlier) and i+2 (issued now) are in flight
-        if (tile + 2 < ntiles) load_tile(tile + 2, tile_c);
-        fast_tile(tile, tile_a);
+        // tile i is consumed while tiles i+1 (issued earlier) and i+2 (issued during tile i) are
+        // in flight
+        fast_tile(tile, tile_a, tile_c);
         wait_ahead(tile + 1 < ntiles, tile + 2 < ntiles);
         lds_barrier();
         if (tile + 1 >= ntiles) break;
-        if (tile + 3 < ntiles) load_tile(tile + 3, tile_a);
-        fast_tile(tile + 1, tile_b);
+        fast_tile(tile + 1, tile_b, tile_a);
         wait_ahead(tile + 2 < ntiles, tile + 3 < ntiles);
         lds_barrier();
         if (tile + 2 >= ntiles) break;
-        if (tile + 4 < ntiles) load_tile(tile + 4, tile_b);
-        fast_tile(tile + 2, tile_c);
+        fast_tile(tile + 2, tile_c, tile_b);
         wait_ahead(tile + 3 < ntiles, tile + 4 < ntiles);
         lds_barrier();
     }
