@@ -43,7 +43,13 @@ DEFAULT_WORKLOAD = "decode-B64-ctx8192"
 CPU_SAMPLE = {"tiny-prefill-L1024": 1024, "decode-B64-ctx8192": 64, "prefill-L16384": 48,
               "mtp-decode-B32x2-ctx65536-paged": 24, "ragged-decode-B16-paged": 16}
 
-KERNEL_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "sparse_mla": "sparse_mla.hip"}
+KERNEL_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "sparse_mla": "sparse_mla.hip",
+                 "write_path": "cache_write.hip"}
+
+# Rotated spans used for the write-path measurement: the indexer key's first 64 of 128 dims, and
+# the latent row's decoupled channel (the 64 dims after the 512 latent dims), adjacent pairs, base 1e4.
+WRITE_K_ROPE = (0, 64, True, 10000.0)
+WRITE_LAT_ROPE = (512, 64, True, 10000.0)
 
 
 def parse():
@@ -55,8 +61,12 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check before timing")
-    ap.add_argument("--stage", default="all", choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy"],
+    ap.add_argument("--stage", default="all",
+                    choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy", "write_path"],
                     help="profiling aid: run only this stage --steps times (no JSON line)")
+    ap.add_argument("--write-path", action="store_true",
+                    help="measure the cache write path (query rotation + key / latent append) of the workload's "
+                         "query tokens instead of the forward; prints its own JSON line")
     return ap.parse_args()
 
 
@@ -84,6 +94,15 @@ def algorithmic(p, stage):
         return kbytes + qbytes + sbytes, flops
     if stage == "topk":
         return int(n[long_].sum()) * 4 + s.T * k * 4, 0
+    if stage == "write_path":
+        # every query token: its indexer key and latent row appended (sources bf16), its query
+        # block rotated (indexer q bf16 -> the workload's indexer dtype; MLA q: the 64-dim span of
+        # each head read and written in place); plus the seq / pos arrays
+        elt = {"f32": 4, "bf16": 2, "fp8": 1}[s.idx_dtype]
+        fp8s = 4 if s.idx_dtype == "fp8" else 0
+        append = 128 * 2 + 576 * 2 + 8 + 128 * elt + fp8s + 576 * 2
+        queries = 4 + HI * (128 * 2 + 128 * elt + fp8s) + H * 64 * 2 * 2
+        return s.T * (append + queries), 0
     if stage == "sparse_mla":
         cnt = np.minimum(n, k)
         gather = int(cnt.sum()) * (576 * 2 + 4)
@@ -158,6 +177,9 @@ def main():
     scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=dev)
     mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, k, H)
     mla_ws = torch.empty(max(1, mla_ws_n), dtype=torch.uint8, device=dev)
+
+    if args.write_path or args.stage == "write_path":
+        return write_path_bench(args, spec, p, dp, dev, stream)
 
     def forward():
         dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, k, dp.q_mla, dp.latent, b, spec.softmax_scale,
@@ -315,6 +337,109 @@ def main():
         "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
         "spot_check": check,
         "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def write_path_bench(args, spec, p, dp, dev, stream):
+    """The cache write path for the workload's query tokens: dsa_rope_queries (indexer q to the
+    workload's indexer dtype, MLA q rotated in place) + dsa_cache_append (indexer key and latent row
+    of each token, at its position)."""
+    import torch
+    import oracle
+    from sparse_attention_sum_amd import dsa
+
+    T, HI, H = spec.T, spec.idx_heads, spec.mla_heads
+    g = torch.Generator(device=dev).manual_seed(1234)
+    seq = torch.from_numpy(p.q_seq.astype(np.int32)).to(dev)
+    pos = torch.from_numpy((p.q_len - 1).astype(np.int32)).to(dev)
+    k_new = torch.randn((T, 128), generator=g, device=dev).to(torch.bfloat16)
+    lat_new = (torch.randn((T, 576), generator=g, device=dev) / 24).to(torch.bfloat16)
+    qi_in = torch.randn((T, HI, 128), generator=g, device=dev).to(torch.bfloat16)
+    odt = {"fp8": torch.uint8, "bf16": torch.int16, "f32": torch.float32}[spec.idx_dtype]
+    qi_out = torch.empty((T, HI, 128), dtype=odt, device=dev)
+    qi_scale = torch.empty((T, HI), dtype=torch.float32, device=dev) if spec.idx_dtype == "fp8" else None
+    qm = dp.q_mla.clone()
+    # the caches of the workload (copies: the forward inputs stay as they are)
+    kc = dsa.Cache(dp.k_cache.data.clone(), None if dp.k_cache.scale is None else dp.k_cache.scale.clone(),
+                   seq_stride=dp.k_cache.seq_stride, page_table=dp.k_cache.page_table, page_size=dp.k_cache.page_size,
+                   dtype=dp.k_cache.dtype)
+    lc = dsa.Cache(dp.latent.data.clone(), None, seq_stride=dp.latent.seq_stride, page_table=dp.latent.page_table,
+                   page_size=dp.latent.page_size, dtype=dp.latent.dtype)
+    kr, lr = dsa.Rope(*WRITE_K_ROPE), dsa.Rope(*WRITE_LAT_ROPE)
+
+    def step():
+        dsa.dsa_rope_queries(qi_in, qi_out, qi_scale, qm, pos, kr, lr, stream=stream)
+        dsa.dsa_cache_append(k_new, lat_new, seq, pos, spec.B, kc, lc, kr, lr, stream=stream)
+
+    flush_buf = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if not args.no_flush:
+            torch.sum(flush_buf, dim=0, keepdim=True, out=flush_out)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    if args.stage == "write_path":
+        print(json.dumps({"stage": "write_path", "workload": args.workload, "mean_us": float(ms.mean() * 1e3)}))
+        return
+    us = float(ms.mean() * 1e3)
+    nbytes, _ = algorithmic(p, "write_path")
+    achieved = nbytes / (us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("write_path", args.workload),
+                "kernel": "write_path"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's write functions on a bounded sample of the same tokens
+        rows = np.unique(np.linspace(0, T - 1, num=min(T, 16)).astype(np.int64))
+        rsel = torch.from_numpy(rows).to(dev)
+        kx = k_new[rsel].view(torch.int16).cpu().numpy().view(np.uint16)
+        lx = lat_new[rsel].view(torch.int16).cpu().numpy().view(np.uint16)
+        qx = qi_in[rsel].view(torch.int16).cpu().numpy().view(np.uint16)
+        qmx = qm[rsel].view(torch.int16).cpu().numpy().view(np.uint16)
+        psel = (p.q_len[rows] - 1).astype(np.int32)
+        krt = (WRITE_K_ROPE[0], WRITE_K_ROPE[1], int(WRITE_K_ROPE[2]), WRITE_K_ROPE[3])
+        lrt = (WRITE_LAT_ROPE[0], WRITE_LAT_ROPE[1], int(WRITE_LAT_ROPE[2]), WRITE_LAT_ROPE[3])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.rope_store(qx, "bf16", psel, krt, spec.idx_dtype)
+            oracle.rope_store(qmx, "bf16", psel, lrt, "bf16")
+            oracle.rope_store(kx[:, None], "bf16", psel, krt, spec.idx_dtype)
+            oracle.rope_store(lx[:, None], "bf16", psel, lrt, "bf16")
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 5.0 or reps >= 200:
+                break
+        cpu = {"value": round(reps * len(rows) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{len(rows)} of {T} tokens of {args.workload} (evenly spaced): the oracle's rotation and "
+                         f"storage of each token's queries and cache rows, {reps} repetition(s) in {dt:.2f} s"}
+    line = {
+        "metric": "cache write path tokens/s (query rotation + key / latent append)",
+        "value": round(T / (us * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "indexer_heads": HI, "mla_heads": H,
+                   "indexer_out": spec.idx_dtype, "k_rope": list(WRITE_K_ROPE), "latent_rope": list(WRITE_LAT_ROPE),
+                   "paged": spec.paged, "cache_state": "hot" if args.no_flush else "flushed between steps"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "alg_bytes": nbytes,
+        "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
     }
     print(json.dumps(line), flush=True)
 

@@ -137,6 +137,58 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        const dsa_batch* batch, int32_t* indices_out, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- cache write path -------------------------------------------------------------------------
+ * The step before the three above: page "一文讀懂DeepSeek-V3.2核心技術DSA", "DSA 的四步工作流程",
+ * first step (the query and key projections carry rotary position information); page "DeepSeek
+ * 稀疏注意力路线", section "DeepSeek-V3：MLA 基座", "核心机制（直觉）" (MLA's position information
+ * travels in a decoupled channel: the 64 dims after the 512 latent dims of a row) and "两阶段流程"
+ * item 1 (the indexer runs in fp8).  The pages give no rotation formula; the standard one is used.
+ *
+ * Numerics: each rotated value is computed in double (angle, cosine, sine, rotation) and rounded once
+ * to binary32; that value is stored as f32, as bf16 (round to nearest even), or as e4m3 with one scale
+ * per 128-wide row: s = max(amax, 1e-12) / 448 (binary32), code = e4m3(x / s) rounded to nearest
+ * even and saturating at 448.  Elements outside the rotated span are converted the same way. */
+
+/* Rotation of the span [offset, offset + dim) of a row: pair i turns by position * base^(-2i/dim)
+ * radians; the pairs are (offset + 2i, offset + 2i + 1) when interleaved, else (offset + i,
+ * offset + i + dim/2).  dim == 0 (or a NULL dsa_rope*) turns the rotation off. */
+typedef struct {
+    int32_t offset;        /* first rotated element of a row */
+    int32_t dim;           /* rotated elements, even */
+    int32_t interleaved;   /* 1: adjacent pairs; 0: the two halves of the span */
+    double base;           /* > 0 and finite */
+} dsa_rope;
+
+/* Append num_tokens new tokens to the indexer key cache and to the latent cache.
+ *   k_new        [num_tokens][128] F32 or BF16 (un-rotated indexer keys), or NULL (k_cache untouched)
+ *   latent_new   [num_tokens][576] F32 or BF16 (un-rotated latent rows), or NULL (latent_cache untouched)
+ *   seq, pos     device [num_tokens]: token i is position pos[i] of sequence seq[i]
+ *   num_seqs     sequences addressable through the caches (the page tables have num_seqs rows)
+ *   k_rope, latent_rope  rotations of the two rows (for DeepSeek-V3.2's latent: offset 512, dim 64)
+ *   k_cache      the 128-dim indexer key cache (F32, BF16, or FP8_E4M3 with a writable scale array);
+ *   latent_cache the 576-dim BF16 latent cache; the `data` (and fp8 `scale`) arrays of both are WRITTEN
+ * Token i goes to the row its layout assigns to (seq[i], pos[i]), rotated at position pos[i].  A token
+ * whose sequence is outside [0, num_seqs), whose position is negative or past its sequence's rows
+ * (contiguous: seq_stride; paged: page_table_stride pages), whose page number is negative, or whose
+ * row is outside [0, num_rows) is not written.  Two tokens of one call must not share a row. */
+dsa_status dsa_cache_append(const void* k_new, int32_t k_new_dtype, const void* latent_new,
+                            int32_t latent_new_dtype, const int32_t* seq, const int32_t* pos,
+                            int32_t num_tokens, int32_t num_seqs, const dsa_rope* k_rope,
+                            const dsa_rope* latent_rope, const dsa_cache* k_cache,
+                            const dsa_cache* latent_cache, hipStream_t stream);
+
+/* Rotate the query blocks of num_tokens tokens at positions pos (device [num_tokens]).
+ *   q_idx_in     [num_tokens][idx_heads][128] F32 or BF16, or NULL (indexer queries skipped)
+ *   q_idx_out    [num_tokens][idx_heads][128] in q_idx_out_dtype (F32, BF16 or FP8_E4M3);
+ *                for FP8_E4M3, q_idx_scale_out [num_tokens][idx_heads] receives the row scales
+ *                (the q_scale of dsa_indexer_scores)
+ *   q_mla        [num_tokens][n_heads][576] BF16, rotated IN PLACE on mla_rope's span only, or NULL
+ * 1 <= idx_heads, n_heads <= 128.  q_idx_out must not overlap q_idx_in. */
+dsa_status dsa_rope_queries(const void* q_idx_in, int32_t q_idx_in_dtype, int32_t idx_heads, void* q_idx_out,
+                            int32_t q_idx_out_dtype, float* q_idx_scale_out, const dsa_rope* idx_rope,
+                            void* q_mla, int32_t n_heads, const dsa_rope* mla_rope, const int32_t* pos,
+                            int32_t num_tokens, hipStream_t stream);
+
 /* Operations for dsa_workspace_size. */
 enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
 

@@ -9,7 +9,10 @@ Each function follows the definition cited in ``oracle.c``:
   * ``topk``        the k best positions per query, ties to the lower position, all when n <= k;
   * ``sparse_mla``  softmax attention of each head over the selected latent rows (MQA form);
   * ``forward``     the three in sequence; the indexer is skipped where n <= k since the selection
-                    then does not depend on it.
+                    then does not depend on it;
+  * ``rope_rows``, ``rope_store``, ``cache_append``, ``bf16_encode``, ``e4m3_encode``: the cache
+                    write path (rotary embedding in double, one rounding to binary32, then bf16 or
+                    per-row-scaled fp8 storage, and the paged / contiguous append).
 """
 from __future__ import annotations
 
@@ -56,6 +59,14 @@ def lib() -> ctypes.CDLL:
         _lib.orc_topk.argtypes = [P, I64, I32, P, P, I32, P, ctypes.c_int]
         _lib.orc_sparse_mla.argtypes = [P, I32, I32, I32, I32, P, I64, P, I32, I32,
                                         P, P, P, I32, P, I32, D, P, P, ctypes.c_int]
+        _lib.orc_bf16_encode.argtypes = [ctypes.c_float]
+        _lib.orc_bf16_encode.restype = ctypes.c_uint16
+        _lib.orc_e4m3_encode.argtypes = [D]
+        _lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        I = ctypes.c_int
+        _lib.orc_rope_rows.argtypes = [P, I, I64, I, P, I, I, I, D, P]
+        _lib.orc_rope_store.argtypes = [P, I, I64, I, I, P, I, I, I, D, P, I, P]
+        _lib.orc_cache_append.argtypes = [P, I, I32, I, P, P, I32, I, I, I, D, P, I, P, I64, I64, P, I32, I32]
     return _lib
 
 
@@ -158,3 +169,67 @@ def forward(q_idx, q_idx_dtype, q_idx_scale, w, k_idx, k_idx_dtype, k_idx_scale,
                           page_table=page_table, page_size=page_size, softmax_scale=softmax_scale,
                           d_v=d_v, qsel=sel, nthreads=nthreads)
     return idx, out, lse
+
+
+# --------------------------------------------------------------------------------------------
+# cache write path
+
+
+def bf16_encode(x) -> np.ndarray:
+    """bf16 codes (uint16) nearest to binary32 values, ties to the even code."""
+    x = np.asarray(x, dtype=np.float32)
+    f = lib().orc_bf16_encode
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """e4m3fn codes (uint8) nearest to values, ties to the even code, saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    f = lib().orc_e4m3_encode
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def _rope_args(rope):
+    off, d, inter, base = rope if rope is not None else (0, 0, 1, 10000.0)
+    return int(off), int(d), int(inter), float(base)
+
+
+def rope_rows(x, src_dtype: str, pos, rope) -> np.ndarray:
+    """Rows x [R, width] (f32 array or bf16 bits) rotated at positions pos [R] in double, rounded
+    once to float32.  rope = (offset, dim, interleaved, base)."""
+    x = _c(x)
+    R, width = x.shape
+    pos = _c(pos, np.int32)
+    out = np.empty((R, width), dtype=np.float32)
+    lib().orc_rope_rows(_ptr(x), DTYPE_CODE[src_dtype], R, width, _ptr(pos), *_rope_args(rope), _ptr(out))
+    return out
+
+
+def rope_store(x, src_dtype: str, pos, rope, dst_dtype: str):
+    """Rows x [T, heads, width] rotated at the token positions pos [T] and stored in dst_dtype.
+    Returns (stored rows [T, heads, width] as f32 / bf16 bits / e4m3 bits, scales [T, heads] or None)."""
+    x = _c(x)
+    T, heads, width = x.shape
+    pos = _c(pos, np.int32)
+    npdt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dst_dtype]
+    out = np.zeros((T, heads, width), dtype=npdt)
+    scale = np.zeros((T, heads), dtype=np.float32) if dst_dtype == "fp8" else None
+    lib().orc_rope_store(_ptr(x), DTYPE_CODE[src_dtype], T * heads, width, heads, _ptr(pos), *_rope_args(rope),
+                         _ptr(out), DTYPE_CODE[dst_dtype], _ptr(scale))
+    return out, scale
+
+
+def cache_append(x, src_dtype: str, seq, pos, num_seqs: int, rope, cache, cache_dtype: str, cache_scale=None,
+                 *, seq_stride=0, page_table=None, page_size=64):
+    """Append rows x [T, width] to `cache` ([rows, width] numpy storage, modified in place; fp8
+    scales go to cache_scale [rows]).  Tokens that map outside the cache are not written."""
+    x = _c(x)
+    T, width = x.shape
+    assert cache.flags["C_CONTIGUOUS"] and cache.shape[1] == width
+    seq = _c(seq, np.int32); pos = _c(pos, np.int32)
+    pt = _c(page_table, np.int32)
+    lib().orc_cache_append(_ptr(x), DTYPE_CODE[src_dtype], T, width, _ptr(seq), _ptr(pos), int(num_seqs),
+                           *_rope_args(rope), _ptr(cache), DTYPE_CODE[cache_dtype], _ptr(cache_scale),
+                           cache.shape[0], int(seq_stride), _ptr(pt), 0 if pt is None else pt.shape[1],
+                           int(page_size))
+    return cache

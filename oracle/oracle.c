@@ -325,3 +325,149 @@ int orc_sparse_mla(const uint16_t* q, int32_t T, int32_t H, int32_t Dqk, int32_t
     orc_parallel(mla_one, &m, qsel ? nsel : T, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* 4. cache write path: rotary position embedding, quantisation and cache append               */
+/*
+ * Rotary embedding (page "一文讀懂DeepSeek-V3.2核心技術DSA", "DSA 的四步工作流程", first step: the
+ * query and key projections carry rotary position information; page "DeepSeek 稀疏注意力路线",
+ * section "DeepSeek-V3：MLA 基座", subsection "核心机制（直觉）": MLA's position information travels in a channel
+ * of its own, the 64 dims after the 512 latent dims).  The pages give no formula; this is the
+ * standard rotation: pair i of the rotated span [off, off + d) of a row at position p turns by the
+ * angle p * base^(-2i/d),
+ *     x_a' = x_a cos - x_b sin,   x_b' = x_a sin + x_b cos,
+ * with the pair (a, b) = (off + 2i, off + 2i + 1) (interleaved) or (off + i, off + i + d/2) (split).
+ * Everything is computed in double; each result is then rounded once to binary32 (round to nearest
+ * even), and that value is stored:
+ *   f32  as is;
+ *   bf16 round to nearest, ties to the even code;
+ *   fp8  one scale per row (the 1x128 per-token tile of the page on the V3 report), s = max(amax,
+ *        1e-12) / 448 in binary32 arithmetic, amax the largest |value| of the row; code = the e4m3
+ *        value nearest to x / s (binary32 division), ties to the even code, |x / s| > 448 saturating
+ *        to 448; a negative value (or -0) keeps the sign bit.
+ */
+
+/* bf16 code nearest to a binary32 value (finite): the two codes around it by truncation of the
+   magnitude, then the nearer one, the even one on a tie. */
+uint16_t orc_bf16_encode(float x) {
+    uint32_t bits;
+    memcpy(&bits, &x, 4);
+    uint16_t lo = (uint16_t)(bits >> 16), hi = (uint16_t)(lo + 1);   /* same sign, next magnitude */
+    double v = (double)x, vl = orc_bf16_value(lo), vh = orc_bf16_value(hi);
+    double dl = fabs(v - vl), dh = fabs(vh - v);
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+/* e4m3 code nearest to a value, by search over the 127 finite magnitudes; ties to the even code;
+   magnitudes above 448 saturate to 448. */
+uint8_t orc_e4m3_encode(double x) {
+    const int neg = signbit(x) ? 1 : 0;
+    const double a = fabs(x);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7e; c++) {
+        const double d = fabs(orc_e4m3_value((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
+    }
+    if (a > 448.0) best = 0x7e;
+    return (uint8_t)(neg ? (best | 0x80) : best);
+}
+
+/* Rotate a row (values in double) in place at position p. */
+static void rope_row(double* x, int width, int64_t p, int off, int d, int interleaved, double base) {
+    if (d <= 0) return;
+    double* y = (double*)malloc(sizeof(double) * (size_t)width);
+    memcpy(y, x, sizeof(double) * (size_t)width);
+    for (int i = 0; i < d / 2; i++) {
+        const int a = interleaved ? off + 2 * i : off + i;
+        const int b = interleaved ? off + 2 * i + 1 : off + i + d / 2;
+        const double ang = (double)p * pow(base, -2.0 * i / d);
+        const double c = cos(ang), s = sin(ang);
+        y[a] = x[a] * c - x[b] * s;
+        y[b] = x[a] * s + x[b] * c;
+    }
+    memcpy(x, y, sizeof(double) * (size_t)width);
+    free(y);
+}
+
+/* Store a row of binary32 values in dtype at dst (row r of a [rows][width] array); fp8 also
+   writes scale[r]. */
+static void store_row(const float* v, int width, int dtype, void* dst, int64_t r, float* scale) {
+    if (dtype == ORC_F32) {
+        memcpy((float*)dst + r * width, v, sizeof(float) * (size_t)width);
+    } else if (dtype == ORC_BF16) {
+        for (int i = 0; i < width; i++) ((uint16_t*)dst)[r * width + i] = orc_bf16_encode(v[i]);
+    } else {
+        float amax = 0.0f;
+        for (int i = 0; i < width; i++) amax = fmaxf(amax, fabsf(v[i]));
+        const float s = fmaxf(amax, 1e-12f) / 448.0f;
+        for (int i = 0; i < width; i++) ((uint8_t*)dst)[r * width + i] = orc_e4m3_encode((double)(v[i] / s));
+        scale[r] = s;
+    }
+}
+
+/* Rotate rows in double and round to binary32: x [R][width] in src_dtype (f32 / bf16),
+   pos [R] (row r at position pos[r]), out [R][width] floats. */
+int orc_rope_rows(const void* x, int src_dtype, int64_t R, int width, const int32_t* pos, int off, int d,
+                  int interleaved, double base, float* out) {
+    double* row = (double*)malloc(sizeof(double) * (size_t)width);
+    for (int64_t r = 0; r < R; r++) {
+        for (int i = 0; i < width; i++) row[i] = elem_value(x, src_dtype, r * width + i);
+        rope_row(row, width, pos[r], off, d, interleaved, base);
+        for (int i = 0; i < width; i++) out[r * width + i] = (float)row[i];
+    }
+    free(row);
+    return 0;
+}
+
+/* Rotate and store rows: x [R][width] (f32 / bf16) -> dst [R][width] in dst_dtype (f32 / bf16 /
+   fp8 with scale [R]); row r at position pos[r / heads] (heads rows per token). */
+int orc_rope_store(const void* x, int src_dtype, int64_t R, int width, int heads, const int32_t* pos,
+                   int off, int d, int interleaved, double base, void* dst, int dst_dtype, float* scale) {
+    double* row = (double*)malloc(sizeof(double) * (size_t)width);
+    float* v = (float*)malloc(sizeof(float) * (size_t)width);
+    for (int64_t r = 0; r < R; r++) {
+        for (int i = 0; i < width; i++) row[i] = elem_value(x, src_dtype, r * width + i);
+        rope_row(row, width, pos[r / heads], off, d, interleaved, base);
+        for (int i = 0; i < width; i++) v[i] = (float)row[i];
+        store_row(v, width, dst_dtype, dst, r, scale);
+    }
+    free(row); free(v);
+    return 0;
+}
+
+/* Append T tokens to a cache: token i of sequence seq[i] at position pos[i] goes to the storage
+   row that the cache layout assigns to it (contiguous: seq * seq_stride + pos; paged: through the
+   page table), rotated and stored in the cache's dtype.  A token whose sequence is outside
+   [0, num_seqs), whose position is negative or past its sequence's rows (contiguous: seq_stride;
+   paged: the page table's width), or whose row falls outside [0, num_rows) is not written. */
+int orc_cache_append(const void* x, int src_dtype, int32_t T, int width, const int32_t* seq,
+                     const int32_t* pos, int32_t num_seqs, int off, int d, int interleaved, double base,
+                     void* cache, int cache_dtype, float* cache_scale, int64_t num_rows, int64_t seq_stride,
+                     const int32_t* page_table, int32_t pt_stride, int32_t page_size) {
+    double* row = (double*)malloc(sizeof(double) * (size_t)width);
+    float* v = (float*)malloc(sizeof(float) * (size_t)width);
+    for (int32_t i = 0; i < T; i++) {
+        const int32_t b = seq[i], p = pos[i];
+        if (b < 0 || b >= num_seqs || p < 0) continue;
+        int64_t r;
+        if (page_table == NULL) {
+            if (p >= seq_stride) continue;
+            r = (int64_t)b * seq_stride + p;
+        } else {
+            if (p / page_size >= pt_stride) continue;
+            const int64_t page = page_table[(int64_t)b * pt_stride + p / page_size];
+            if (page < 0) continue;
+            r = page * page_size + p % page_size;
+        }
+        if (r >= num_rows) continue;
+        for (int j = 0; j < width; j++) row[j] = elem_value(x, src_dtype, (int64_t)i * width + j);
+        rope_row(row, width, p, off, d, interleaved, base);
+        for (int j = 0; j < width; j++) v[j] = (float)row[j];
+        store_row(v, width, cache_dtype, cache, r, cache_scale);
+    }
+    free(row); free(v);
+    return 0;
+}

@@ -125,6 +125,37 @@ dsa_status check_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, 
     return DSA_OK;
 }
 
+dsa_status check_rope(const dsa_rope* r, int width, const char* name, dsa::RopeView& v) {
+    v.off = 0; v.dim = 0; v.inter = 1; v.base = 1.0;
+    if (!r || r->dim == 0) return DSA_OK;
+    if (r->dim < 0 || (r->dim & 1) || r->offset < 0 || r->offset + r->dim > width)
+        return fail(DSA_ERR_INVALID_ARG, "%s: span [%d, %d + %d) must be even and inside the row of %d", name,
+                    r->offset, r->offset, r->dim, width);
+    if (!(r->base > 0.0) || !std::isfinite(r->base)) return fail(DSA_ERR_INVALID_ARG, "%s: base must be positive and finite", name);
+    v.off = r->offset; v.dim = r->dim; v.inter = r->interleaved ? 1 : 0; v.base = r->base;
+    return DSA_OK;
+}
+
+// A cache that the write path fills: layout fields only (the readers' max_len checks do not apply).
+dsa_status check_write_cache(const dsa_cache* c, int dim, const char* name) {
+    if (!c) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!c->data) return fail(DSA_ERR_INVALID_ARG, "%s: data is NULL", name);
+    if (c->dim != dim) return fail(DSA_ERR_UNSUPPORTED, "%s: dim %d, expected %d", name, c->dim, dim);
+    if (c->dtype != DSA_F32 && c->dtype != DSA_BF16 && c->dtype != DSA_FP8_E4M3)
+        return fail(DSA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, c->dtype);
+    if (c->dtype == DSA_FP8_E4M3 && !c->scale) return fail(DSA_ERR_INVALID_ARG, "%s: fp8 cache needs a scale array", name);
+    if (c->num_rows < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_rows < 0", name);
+    if (c->page_table) {
+        if (c->page_size < 1 || c->page_table_stride < 1)
+            return fail(DSA_ERR_INVALID_ARG, "%s: page_size and page_table_stride must be >= 1", name);
+    } else if (c->seq_stride < 0) {
+        return fail(DSA_ERR_INVALID_ARG, "%s: seq_stride < 0", name);
+    }
+    return DSA_OK;
+}
+
+bool src_dtype_ok(int32_t d) { return d == DSA_F32 || d == DSA_BF16; }
+
 }  // namespace
 
 extern "C" {
@@ -244,6 +275,70 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
     return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
                                              (uint16_t*)out, lse, mla_ws, stream),
                       "forward: sparse_mla launch");
+}
+
+dsa_status dsa_cache_append(const void* k_new, int32_t k_new_dtype, const void* latent_new,
+                            int32_t latent_new_dtype, const int32_t* seq, const int32_t* pos,
+                            int32_t num_tokens, int32_t num_seqs, const dsa_rope* k_rope,
+                            const dsa_rope* latent_rope, const dsa_cache* k_cache,
+                            const dsa_cache* latent_cache, hipStream_t stream) {
+    if (num_tokens < 0 || num_seqs < 0) return fail(DSA_ERR_INVALID_ARG, "cache_append: num_tokens or num_seqs < 0");
+    if (num_tokens > 0 && (!seq || !pos)) return fail(DSA_ERR_INVALID_ARG, "cache_append: seq or pos is NULL");
+    dsa::RopeView kr, lr;
+    dsa_status s = check_rope(k_rope, dsa::kIdxDim, "k_rope", kr);
+    if (s != DSA_OK) return s;
+    s = check_rope(latent_rope, dsa::kDqk, "latent_rope", lr);
+    if (s != DSA_OK) return s;
+    dsa::CacheView kc{}, lc{};
+    int kc_dtype = DSA_F32;
+    if (k_new) {
+        if (!src_dtype_ok(k_new_dtype)) return fail(DSA_ERR_UNSUPPORTED, "cache_append: k_new dtype must be F32 or BF16");
+        s = check_write_cache(k_cache, dsa::kIdxDim, "k_cache");
+        if (s != DSA_OK) return s;
+        kc = view(k_cache);
+        kc_dtype = k_cache->dtype;
+    }
+    if (latent_new) {
+        if (!src_dtype_ok(latent_new_dtype))
+            return fail(DSA_ERR_UNSUPPORTED, "cache_append: latent_new dtype must be F32 or BF16");
+        s = check_write_cache(latent_cache, dsa::kDqk, "latent_cache");
+        if (s != DSA_OK) return s;
+        if (latent_cache->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "cache_append: latent cache must be bf16");
+        lc = view(latent_cache);
+    }
+    if (!k_new && !latent_new) return DSA_OK;
+    return hip_status(dsa::launch_cache_append(k_new, k_new_dtype, latent_new, latent_new_dtype, seq, pos, num_tokens,
+                                               num_seqs, kr, lr, kc, kc_dtype, lc, stream),
+                      "cache_append launch");
+}
+
+dsa_status dsa_rope_queries(const void* q_idx_in, int32_t q_idx_in_dtype, int32_t idx_heads, void* q_idx_out,
+                            int32_t q_idx_out_dtype, float* q_idx_scale_out, const dsa_rope* idx_rope,
+                            void* q_mla, int32_t n_heads, const dsa_rope* mla_rope, const int32_t* pos,
+                            int32_t num_tokens, hipStream_t stream) {
+    if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "rope_queries: num_tokens < 0");
+    if (num_tokens > 0 && !pos) return fail(DSA_ERR_INVALID_ARG, "rope_queries: pos is NULL");
+    dsa::RopeView ri, rm;
+    dsa_status s = check_rope(idx_rope, dsa::kIdxDim, "idx_rope", ri);
+    if (s != DSA_OK) return s;
+    s = check_rope(mla_rope, dsa::kDqk, "mla_rope", rm);
+    if (s != DSA_OK) return s;
+    if (q_idx_in) {
+        if (!src_dtype_ok(q_idx_in_dtype)) return fail(DSA_ERR_UNSUPPORTED, "rope_queries: q_idx_in dtype must be F32 or BF16");
+        if (q_idx_out_dtype != DSA_F32 && q_idx_out_dtype != DSA_BF16 && q_idx_out_dtype != DSA_FP8_E4M3)
+            return fail(DSA_ERR_INVALID_ARG, "rope_queries: unknown q_idx_out dtype %d", q_idx_out_dtype);
+        if (!q_idx_out) return fail(DSA_ERR_INVALID_ARG, "rope_queries: q_idx_out is NULL");
+        if (q_idx_out_dtype == DSA_FP8_E4M3 && !q_idx_scale_out)
+            return fail(DSA_ERR_INVALID_ARG, "rope_queries: fp8 output needs q_idx_scale_out");
+        if (idx_heads < 1 || idx_heads > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "rope_queries: idx_heads %d not in [1,128]", idx_heads);
+    }
+    if (q_mla && (n_heads < 1 || n_heads > kMaxHeads))
+        return fail(DSA_ERR_UNSUPPORTED, "rope_queries: n_heads %d not in [1,128]", n_heads);
+    if (!q_idx_in && (!q_mla || rm.dim == 0)) return DSA_OK;
+    return hip_status(dsa::launch_rope_queries(q_idx_in, q_idx_in_dtype, q_idx_in ? idx_heads : 0, q_idx_out,
+                                               q_idx_out_dtype, q_idx_scale_out, ri, (uint16_t*)q_mla,
+                                               q_mla ? n_heads : 0, rm, pos, num_tokens, stream),
+                      "rope_queries launch");
 }
 
 }  // extern "C"

@@ -30,4 +30,21 @@ hipError_t launch_sparse_mla(const uint16_t* q, int H, const CacheView& lat, con
                              const int32_t* idx, int k, float softmax_scale, uint16_t* out, float* lse,
                              void* ws, hipStream_t st);
 
+// Rotary embedding of the span [off, off + dim) of a row (dim == 0: no rotation); pair i turns by
+// position * base^(-2i/dim), pairs (off + 2i, off + 2i + 1) when inter, else (off + i, off + i + dim/2).
+struct RopeView {
+    int off, dim, inter;
+    double base;
+};
+
+// Cache write path: rotate, store in the caches' formats and append new tokens (either source may be
+// null); rotate the query blocks (indexer out of place, MLA in place on its span).
+hipError_t launch_cache_append(const void* k_new, int k_dtype, const void* lat_new, int lat_dtype,
+                               const int32_t* seq, const int32_t* pos, int T, int num_seqs, const RopeView& k_rope,
+                               const RopeView& lat_rope, const CacheView& kc, int kc_dtype, const CacheView& lc,
+                               hipStream_t st);
+hipError_t launch_rope_queries(const void* qi_in, int qi_dtype, int Hi, void* qi_out, int qo_dtype, float* qo_scale,
+                               const RopeView& ri, uint16_t* qm, int Hm, const RopeView& rm, const int32_t* pos,
+                               int T, hipStream_t st);
+
 }  // namespace dsa

@@ -23,7 +23,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_workspace_size",
-           "dsa_status_string", "dsa_last_error", "dsa_version")
+           "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries")
 
 
 class DsaError(RuntimeError):
@@ -43,6 +43,24 @@ class _Batch(ctypes.Structure):
     _fields_ = [("num_queries", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("cu_q", ctypes.c_void_p),
                 ("q_seq", ctypes.c_void_p), ("q_len", ctypes.c_void_p), ("max_len", ctypes.c_int32),
                 ("max_q", ctypes.c_int32)]
+
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int32), ("dim", ctypes.c_int32), ("interleaved", ctypes.c_int32),
+                ("base", ctypes.c_double)]
+
+
+@dataclasses.dataclass
+class Rope:
+    """Rotation of the span [offset, offset + dim) of a row: pair i turns by position * base^(-2i/dim);
+    pairs are adjacent (interleaved) or the two halves of the span."""
+    offset: int = 0
+    dim: int = 0
+    interleaved: bool = True
+    base: float = 10000.0
+
+    def struct(self) -> _Rope:
+        return _Rope(int(self.offset), int(self.dim), 1 if self.interleaved else 0, float(self.base))
 
 
 _lib = None
@@ -67,12 +85,16 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_mla.argtypes = [P, I32, I32, I32, CP, BP, P, I32, F, P, P, P, ctypes.c_size_t, P]
     L.dsa_forward.argtypes = [P, I32, P, P, I32, CP, F, I32, P, I32, CP, F, BP, P, P, P, P, ctypes.c_size_t, P]
     L.dsa_workspace_size.argtypes = [I32, BP, I32, I32, I32]
+    RP = ctypes.POINTER(_Rope)
+    L.dsa_cache_append.argtypes = [P, I32, P, I32, P, P, I32, I32, RP, RP, CP, CP, P]
+    L.dsa_rope_queries.argtypes = [P, I32, I32, P, I32, P, RP, P, I32, RP, P, I32, P]
     L.dsa_workspace_size.restype = ctypes.c_size_t
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
-    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward"):
+    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_cache_append",
+                 "dsa_rope_queries"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -212,3 +234,36 @@ def dsa_forward(q_idx: torch.Tensor, q_idx_scale: Optional[torch.Tensor], weight
                                float(softmax_scale), ctypes.byref(b), _ptr(indices_out), _ptr(out), _ptr(lse),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse, indices_out
+
+
+def dsa_cache_append(k_new: Optional[torch.Tensor], latent_new: Optional[torch.Tensor], seq: torch.Tensor,
+                     pos: torch.Tensor, num_seqs: int, k_cache: Optional[Cache], latent: Optional[Cache],
+                     k_rope: Optional[Rope] = None, latent_rope: Optional[Rope] = None, stream=None):
+    """Rotate new tokens' indexer keys [T, 128] and latent rows [T, 576] (f32 or bf16) at positions pos
+    [T] and write them into the caches (token i at position pos[i] of sequence seq[i])."""
+    T = int(seq.shape[0])
+    kc = None if k_cache is None else k_cache.struct()
+    lc = None if latent is None else latent.struct()
+    kr = None if k_rope is None else k_rope.struct()
+    lr = None if latent_rope is None else latent_rope.struct()
+    _check(load().dsa_cache_append(_ptr(k_new), DSA_F32 if k_new is None else dtype_code(k_new), _ptr(latent_new),
+                                   DSA_F32 if latent_new is None else dtype_code(latent_new), _ptr(seq), _ptr(pos),
+                                   T, int(num_seqs), None if kr is None else ctypes.byref(kr),
+                                   None if lr is None else ctypes.byref(lr), None if kc is None else ctypes.byref(kc),
+                                   None if lc is None else ctypes.byref(lc), _stream(stream)))
+
+
+def dsa_rope_queries(q_idx_in: Optional[torch.Tensor], q_idx_out: Optional[torch.Tensor],
+                     q_idx_scale_out: Optional[torch.Tensor], q_mla: Optional[torch.Tensor], pos: torch.Tensor,
+                     idx_rope: Optional[Rope] = None, mla_rope: Optional[Rope] = None, stream=None):
+    """Rotate indexer queries [T, H_I, 128] (f32 / bf16) into q_idx_out (f32 / bf16 / fp8 bits with
+    row scales in q_idx_scale_out [T, H_I]) and MLA queries [T, H, 576] bf16 in place."""
+    T = int(pos.shape[0])
+    ir = None if idx_rope is None else idx_rope.struct()
+    mr = None if mla_rope is None else mla_rope.struct()
+    _check(load().dsa_rope_queries(_ptr(q_idx_in), DSA_F32 if q_idx_in is None else dtype_code(q_idx_in),
+                                   0 if q_idx_in is None else int(q_idx_in.shape[1]), _ptr(q_idx_out),
+                                   DSA_F32 if q_idx_out is None else dtype_code(q_idx_out), _ptr(q_idx_scale_out),
+                                   None if ir is None else ctypes.byref(ir), _ptr(q_mla),
+                                   0 if q_mla is None else int(q_mla.shape[1]),
+                                   None if mr is None else ctypes.byref(mr), _ptr(pos), T, _stream(stream)))

@@ -136,3 +136,53 @@ def test_workspace_sizes(lib):
     assert lib.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512) == 0
     assert lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512) == 0
     assert lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, None, 2048, 128, 512) == 0
+
+
+def _append(lib, k_new=FAKE, k_dtype=dsa.DSA_F32, lat=FAKE, lat_dtype=dsa.DSA_BF16, T=4, B=2, kc=None, lc=None,
+            kr=None, lr=None, seq=FAKE, pos=FAKE):
+    kc = kc or dsa._Cache(FAKE, FAKE, dsa.DSA_FP8_E4M3, 128, 1000, 100, None, 0, 64)
+    lc = lc or dsa._Cache(FAKE, None, dsa.DSA_BF16, 576, 1000, 100, None, 0, 64)
+    return lib.dsa_cache_append(k_new, k_dtype, lat, lat_dtype, seq, pos, T, B,
+                                None if kr is None else ctypes.byref(kr), None if lr is None else ctypes.byref(lr),
+                                ctypes.byref(kc), ctypes.byref(lc), None)
+
+
+def test_cache_append_validation(lib):
+    assert _append(lib, T=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert _append(lib, seq=None) == dsa.DSA_ERR_INVALID_ARG
+    assert _append(lib, k_dtype=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED          # sources are f32 / bf16
+    assert _append(lib, lat_dtype=7) == dsa.DSA_ERR_UNSUPPORTED
+    # fp8 key cache without a scale array
+    assert _append(lib, kc=dsa._Cache(FAKE, None, dsa.DSA_FP8_E4M3, 128, 1000, 100, None, 0, 64)) == dsa.DSA_ERR_INVALID_ARG
+    assert _append(lib, kc=dsa._Cache(FAKE, FAKE, dsa.DSA_FP8_E4M3, 576, 1000, 100, None, 0, 64)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _append(lib, lc=dsa._Cache(FAKE, None, dsa.DSA_F32, 576, 1000, 100, None, 0, 64)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _append(lib, lc=dsa._Cache(FAKE, None, dsa.DSA_BF16, 576, 1000, 100, FAKE, 0, 64)) == dsa.DSA_ERR_INVALID_ARG
+    assert _append(lib, lc=dsa._Cache(None, None, dsa.DSA_BF16, 576, 1000, 100, None, 0, 64)) == dsa.DSA_ERR_INVALID_ARG
+    assert _append(lib, kr=dsa._Rope(0, 63, 1, 10000.0)) == dsa.DSA_ERR_INVALID_ARG   # odd width
+    assert _append(lib, kr=dsa._Rope(100, 64, 1, 10000.0)) == dsa.DSA_ERR_INVALID_ARG  # past the row
+    assert _append(lib, lr=dsa._Rope(512, 64, 1, 0.0)) == dsa.DSA_ERR_INVALID_ARG     # base <= 0
+    assert _append(lib, lr=dsa._Rope(512, 64, 1, float("inf"))) == dsa.DSA_ERR_INVALID_ARG
+    assert b"latent_rope" in lib.dsa_last_error()
+    # nothing to write: returns before any launch
+    assert _append(lib, k_new=None, lat=None, kc=dsa._Cache(), lc=dsa._Cache()) == dsa.DSA_OK
+
+
+def _ropeq(lib, qi=FAKE, qi_dtype=dsa.DSA_BF16, hi=64, qo=FAKE, qo_dtype=dsa.DSA_FP8_E4M3, qs=FAKE, ri=None,
+           qm=FAKE, hm=128, rm=None, pos=FAKE, T=4):
+    return lib.dsa_rope_queries(qi, qi_dtype, hi, qo, qo_dtype, qs, None if ri is None else ctypes.byref(ri), qm, hm,
+                                None if rm is None else ctypes.byref(rm), pos, T, None)
+
+
+def test_rope_queries_validation(lib):
+    assert _ropeq(lib, T=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert _ropeq(lib, pos=None) == dsa.DSA_ERR_INVALID_ARG
+    assert _ropeq(lib, qi_dtype=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED
+    assert _ropeq(lib, qo_dtype=9) == dsa.DSA_ERR_INVALID_ARG
+    assert _ropeq(lib, qs=None) == dsa.DSA_ERR_INVALID_ARG                          # fp8 needs the scales
+    assert _ropeq(lib, qo=None) == dsa.DSA_ERR_INVALID_ARG
+    assert _ropeq(lib, hi=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert _ropeq(lib, hm=129) == dsa.DSA_ERR_UNSUPPORTED
+    assert _ropeq(lib, rm=dsa._Rope(520, 64, 0, 10000.0)) == dsa.DSA_ERR_INVALID_ARG  # past the 576-wide row
+    assert _ropeq(lib, ri=dsa._Rope(-2, 64, 1, 10000.0)) == dsa.DSA_ERR_INVALID_ARG
+    # nothing to do: no indexer queries and an MLA rotation of width 0
+    assert _ropeq(lib, qi=None, rm=dsa._Rope(0, 0, 1, 10000.0)) == dsa.DSA_OK
