@@ -114,6 +114,21 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Selection variants of the top-k step (page "DeepSeek-V3.2推理加速引擎深度剖析", closing outlook:
+ * a K chosen per query, and the sliding-window branch combined with the selection; page
+ * "DeepSeek-V3.2加速技术详解": the third, sliding-window branch).
+ *   k_per_query  device [T] int32, or NULL: query t selects its best min(max(k_per_query[t], 0), k)
+ *                positions (k when NULL) by the order of dsa_topk, or all n_t positions when n_t is
+ *                not larger
+ *   window       W >= 0: the W most recent positions n_t - W .. n_t - 1 join the selection (set union)
+ *   indices      [T][k + window] int32: the union in ascending order, then -1 padding; it feeds
+ *                dsa_sparse_mla with k + window as its k
+ * 1 <= k and k + window <= 65536.  With k_per_query NULL and window 0 this is dsa_topk.  workspace
+ * may be NULL. */
+dsa_status dsa_topk_select(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k,
+                           const int32_t* k_per_query, int32_t window, int32_t* indices, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Sparse MLA in MQA form over the selected latent rows.
  *   q        [T][n_heads][d_qk] bf16 (d_qk = 576)
  *   latent   the latent cache, BF16, dim 576; values are the first d_v = 512 dims of each row

@@ -10,6 +10,7 @@ Each function follows the definition cited in ``oracle.c``:
   * ``sparse_mla``  softmax attention of each head over the selected latent rows (MQA form);
   * ``forward``     the three in sequence; the indexer is skipped where n <= k since the selection
                     then does not depend on it;
+  * ``topk_select``  per-query k and the union with a sliding window of recent positions;
   * ``rope_rows``, ``rope_store``, ``cache_append``, ``bf16_encode``, ``e4m3_encode``: the cache
                     write path (rotary embedding in double, one rounding to binary32, then bf16 or
                     per-row-scaled fp8 storage, and the paged / contiguous append).
@@ -57,6 +58,7 @@ def lib() -> ctypes.CDLL:
                                      P, ctypes.c_int, P, I64, P, I32, I32,
                                      P, P, P, I32, D, P, I64, ctypes.c_int]
         _lib.orc_topk.argtypes = [P, I64, I32, P, P, I32, P, ctypes.c_int]
+        _lib.orc_topk_select.argtypes = [P, I64, I32, P, P, I32, P, I32, P, ctypes.c_int]
         _lib.orc_sparse_mla.argtypes = [P, I32, I32, I32, I32, P, I64, P, I32, I32,
                                         P, P, P, I32, P, I32, D, P, P, ctypes.c_int]
         _lib.orc_bf16_encode.argtypes = [ctypes.c_float]
@@ -122,6 +124,21 @@ def topk(scores, q_len, k, rows=None, nthreads=0):
     rows = _c(rows, np.int32)
     out = np.empty((R, k), dtype=np.int32)
     lib().orc_topk(_ptr(s), int(ld), R, _ptr(q_len), _ptr(rows), int(k), _ptr(out), int(nthreads))
+    return out
+
+
+def topk_select(scores, q_len, k, k_per_query=None, window=0, rows=None, nthreads=0):
+    """Selection variants: query t's best min(max(k_per_query[t], 0), k) positions (k when None; all
+    when n_t is not larger), united with its last `window` positions; int32 [R, k + window] in
+    ascending position order, -1 padded."""
+    s = _c(scores, np.float64)
+    R, ld = s.shape
+    q_len = _c(q_len, np.int32)
+    rows = _c(rows, np.int32)
+    kq = _c(k_per_query, np.int32)
+    out = np.empty((R, k + window), dtype=np.int32)
+    lib().orc_topk_select(_ptr(s), int(ld), R, _ptr(q_len), _ptr(rows), int(k), _ptr(kq), int(window), _ptr(out),
+                          int(nthreads))
     return out
 
 

@@ -249,6 +249,57 @@ int orc_topk(const double* scores, int64_t ld, int32_t R, const int32_t* q_len, 
     return 0;
 }
 
+/* Selection variants (page "DeepSeek-V3.2推理加速引擎深度剖析", closing outlook: a K chosen per
+   query, and the sliding-window branch combined with the selection; page "DeepSeek-V3.2加速技术详解",
+   the third, sliding-window branch): query t takes its own k_t = clamp(kq[t], 0, k) (k when kq is
+   NULL) best positions by the same order (all n_t when n_t <= k_t), and the set union with the W
+   most recent positions n_t - W .. n_t - 1; the result is listed in ascending position order,
+   -1 padded to k + W entries. */
+typedef struct {
+    const double* scores; int64_t ld;
+    const int32_t* q_len; const int32_t* rows;
+    int32_t k; const int32_t* kq; int32_t window;
+    int32_t* idx;
+} select_ctx;
+
+static void select_one(void* p, int64_t r) {
+    select_ctx* c = (select_ctx*)p;
+    const int64_t t = c->rows ? c->rows[r] : r;
+    const int64_t n = c->q_len[t];
+    const int32_t width = c->k + c->window;
+    int64_t kt = c->kq ? c->kq[t] : c->k;
+    if (kt < 0) kt = 0;
+    if (kt > c->k) kt = c->k;
+    const double* row = c->scores + r * c->ld;
+    int32_t* out = c->idx + r * (int64_t)width;
+    char* chosen = (char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    if (n <= kt) {
+        for (int64_t s = 0; s < n; s++) chosen[s] = 1;
+    } else {
+        scored* all = (scored*)malloc(sizeof(scored) * (size_t)n);
+        for (int64_t s = 0; s < n; s++) { all[s].v = row[s]; all[s].s = s; }
+        qsort(all, (size_t)n, sizeof(scored), by_score_then_pos);
+        for (int64_t i = 0; i < kt; i++) chosen[all[i].s] = 1;
+        free(all);
+    }
+    for (int64_t s = n - c->window; s < n; s++)
+        if (s >= 0) chosen[s] = 1;
+    int32_t m = 0;
+    for (int64_t s = 0; s < n; s++)
+        if (chosen[s]) out[m++] = (int32_t)s;
+    for (; m < width; m++) out[m] = -1;
+    free(chosen);
+}
+
+/* scores: [R][ld] doubles, row r of query rows[r] (or r); kq: [T] or NULL; idx: [R][k + window]. */
+int orc_topk_select(const double* scores, int64_t ld, int32_t R, const int32_t* q_len, const int32_t* rows,
+                    int32_t k, const int32_t* kq, int32_t window, int32_t* idx, int nthreads) {
+    select_ctx c;
+    c.scores = scores; c.ld = ld; c.q_len = q_len; c.rows = rows; c.k = k; c.kq = kq; c.window = window; c.idx = idx;
+    orc_parallel(select_one, &c, R, nthreads);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* 3. sparse MLA, MQA form                                                                    */
 

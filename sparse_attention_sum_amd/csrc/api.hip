@@ -219,7 +219,25 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int
     if (batch->num_queries > 0 && (!indices || (!scores && batch->max_len > k)))
         return fail(DSA_ERR_INVALID_ARG, "topk: scores or indices is NULL");
     if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "topk: ld %lld < max_len %d", (long long)ld, batch->max_len);
-    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, indices, stream), "topk launch");
+    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, nullptr, 0, indices, stream), "topk launch");
+}
+
+dsa_status dsa_topk_select(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k,
+                           const int32_t* k_per_query, int32_t window, int32_t* indices, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    dsa_status s = check_batch(batch);
+    if (s != DSA_OK) return s;
+    if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
+    if (window < 0 || (int64_t)k + window > kMaxK)
+        return fail(DSA_ERR_INVALID_ARG, "window %d: must be >= 0 with k + window <= %d", window, kMaxK);
+    if (batch->num_queries > 0 && (!scores || !indices))
+        return fail(DSA_ERR_INVALID_ARG, "topk_select: scores or indices is NULL");
+    if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "topk_select: ld %lld < max_len %d", (long long)ld, batch->max_len);
+    if (batch->num_queries == 0) return DSA_OK;
+    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, k_per_query, window, indices, stream),
+                      "topk_select launch");
 }
 
 dsa_status dsa_sparse_mla(const void* q, int32_t n_heads, int32_t d_qk, int32_t d_v, const dsa_cache* latent,
@@ -270,7 +288,7 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        "forward: indexer launch");
         if (s != DSA_OK) return s;
     }
-    s = hip_status(dsa::launch_topk(scores, ld, bv, k, idx, stream), "forward: topk launch");
+    s = hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, idx, stream), "forward: topk launch");
     if (s != DSA_OK) return s;
     return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
                                              (uint16_t*)out, lse, mla_ws, stream),

@@ -18,9 +18,10 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
                           const CacheView& kc, const BatchView& bv, float scale, float* scores,
                           int64_t ld, int skip_le, hipStream_t st);
 
-// Top-k per query row (ascending positions, -1 padded).
-hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, int32_t* idx,
-                       hipStream_t st);
+// Top-k per query row (ascending positions, -1 padded), rows of k + window entries: query t's best
+// clamp(kq[t], 0, k) positions (k when kq is null) united with its last `window` positions.
+hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, const int32_t* kq, int window,
+                       int32_t* idx, hipStream_t st);
 
 // Sparse MLA.  `splits` partitions the k index slots; partial results go to the workspace when
 // splits > 1.  mla_splits() is the split count the library uses for a batch.

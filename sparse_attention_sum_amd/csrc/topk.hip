@@ -165,7 +165,7 @@ __device__ __forceinline__ uint32_t wave_reduce_min(uint32_t v) {
 template <typename Key4, typename Pos4>
 __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32_t mask, uint32_t thr,
                                         uint32_t need_eq, int k, int32_t* __restrict__ orow,
-                                        uint32_t (&wcnt)[2][kTkWaves]) {
+                                        uint32_t (&wcnt)[2][kTkWaves], int wlo, uint32_t* first_win) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = (((nw + kTkWaves - 1) / kTkWaves) + 255) & ~255;
     const int beg = min(nw, wave * seg), end = min(nw, beg + seg);
@@ -217,7 +217,12 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
                 eq_seen++;
             }
             if (take) {
-                if (at < (uint32_t)k) orow[at] = p[j];
+                if (at < (uint32_t)k) {
+                    // positions in the window [wlo, n) are written with the window block; the
+                    // first of them marks where that block starts
+                    if (p[j] < wlo) orow[at] = p[j];
+                    else atomicMin(first_win, at);
+                }
                 at++;
             }
         }
@@ -227,21 +232,32 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
     }
 }
 
+// Query t selects its best kt = clamp(kq[t], 0, k) positions (k when kq is null; all when n <= kt)
+// and adds its last `window` positions; the union is written in ascending order to a row of
+// `width` = k + window entries, -1 padded.  The plain top-k is kq = null, window = 0.
 __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        BatchView bv, int k, int32_t* __restrict__ out) {
+                                                        BatchView bv, int k, const int32_t* __restrict__ kq,
+                                                        int window, int width, int32_t* __restrict__ out) {
     // cached rows: keys[kCap]; long rows: candidate keys [0, kCandCap) + positions [kCandCap, kCap)
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ uint32_t hist[kHistCopies][kBins];   // copies shared by alternate waves (fewer collisions)
     __shared__ uint32_t red[2][kTkWaves];
     __shared__ uint32_t sel[3];
     __shared__ uint32_t wcnt[2][kTkWaves];
+    __shared__ uint32_t first_win;
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t* orow = out + (int64_t)t * k;
+    int32_t* orow = out + (int64_t)t * width;
     const int n = max(0, min(bv.q_len[t], bv.max_len));
-    if (n <= k) {
-        for (int i = tid; i < k; i += kTkBlock) orow[i] = i < n ? i : -1;
+    const int kt = kq != nullptr ? max(0, min(kq[t], k)) : k;
+    const int wn = min(window, n), wlo = n - wn;   // the window: positions [wlo, n)
+    if (n <= kt) {
+        for (int i = tid; i < width; i += kTkBlock) orow[i] = i < n ? i : -1;
+        return;
+    }
+    if (kt == 0) {
+        for (int i = tid; i < width; i += kTkBlock) orow[i] = i < wn ? wlo + i : -1;
         return;
     }
     const float* srow = scores + (int64_t)t * ld;
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
 
     uint32_t prefix = lo;            // bits resolved so far (under `mask`)
     uint32_t mask = 0xffffffffu;
-    uint32_t remaining = (uint32_t)k; // keys still to take among those matching the prefix
+    uint32_t remaining = (uint32_t)kt; // keys still to take among those matching the prefix
 
     // Ordered gather of the candidates (keys with (key & mask) >= prefix) of a long row into LDS:
     // thread t takes keys [base + 16 t, +16) of each step, a block-wide prefix sum gives their
@@ -419,25 +435,34 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     // exit, where the bin holds exactly `remaining` keys).  (All keys equal: the first k.)
     const uint32_t thr = prefix, need_eq = remaining;
 
-    compact(key4, pos4, nw, mask, thr, need_eq, k, orow, wcnt);
+    if (tid == 0) first_win = (uint32_t)kt;   // ordered before compact's writes by its barrier
+    compact(key4, pos4, nw, mask, thr, need_eq, kt, orow, wcnt, wlo, &first_win);
+    if (wn > 0 || width > kt) {
+        // the selected positions below the window fill slots [0, c); then the window, then padding
+        __syncthreads();
+        const int c = (int)first_win;
+        for (int i = tid; i < width - c; i += kTkBlock) orow[c + i] = i < wn ? wlo + i : -1;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, int32_t* idx,
-                       hipStream_t st) {
+hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, const int32_t* kq, int window,
+                       int32_t* idx, hipStream_t st) {
     if (bv.T == 0) return hipSuccess;
     // LDS for the longest row: its keys (rounded up so whole 16-byte reads stay inside), or the
     // candidate area when rows may exceed the key cache
     size_t words = 0;
-    if (bv.max_len > k) words = bv.max_len > kCap ? (size_t)kLdsWords : (size_t)((bv.max_len + 3) & ~3);
+    // (with a per-query k any query may select, so the key cache is sized for every row)
+    if (bv.max_len > (kq != nullptr ? 0 : k))
+        words = bv.max_len > kCap ? (size_t)kLdsWords : (size_t)((bv.max_len + 3) & ~3);
     const size_t shm = words * sizeof(uint32_t);
     if (shm > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)shm);
         if (e != hipSuccess) return e;
     }
-    topk_kernel<<<bv.T, kTkBlock, shm, st>>>(scores, ld, bv, k, idx);
+    topk_kernel<<<bv.T, kTkBlock, shm, st>>>(scores, ld, bv, k, kq, window, k + window, idx);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_workspace_size",
-           "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries")
+           "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries",
+           "dsa_topk_select")
 
 
 class DsaError(RuntimeError):
@@ -82,6 +83,7 @@ def load() -> ctypes.CDLL:
     CP, BP = ctypes.POINTER(_Cache), ctypes.POINTER(_Batch)
     L.dsa_indexer_scores.argtypes = [P, I32, P, P, I32, I32, CP, BP, F, P, I64, P]
     L.dsa_topk.argtypes = [P, I64, BP, I32, P, P, ctypes.c_size_t, P]
+    L.dsa_topk_select.argtypes = [P, I64, BP, I32, P, I32, P, P, ctypes.c_size_t, P]
     L.dsa_sparse_mla.argtypes = [P, I32, I32, I32, CP, BP, P, I32, F, P, P, P, ctypes.c_size_t, P]
     L.dsa_forward.argtypes = [P, I32, P, P, I32, CP, F, I32, P, I32, CP, F, BP, P, P, P, P, ctypes.c_size_t, P]
     L.dsa_workspace_size.argtypes = [I32, BP, I32, I32, I32]
@@ -94,7 +96,7 @@ def load() -> ctypes.CDLL:
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_cache_append",
-                 "dsa_rope_queries"):
+                 "dsa_rope_queries", "dsa_topk_select"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -193,6 +195,19 @@ def dsa_topk(scores: Optional[torch.Tensor], ld: int, batch: Batch, k: int, indi
         indices = torch.empty((batch.num_queries, k), dtype=torch.int32, device=batch.q_len.device)
     b = batch.struct()
     _check(load().dsa_topk(_ptr(scores), int(ld), ctypes.byref(b), int(k), _ptr(indices), None, 0, _stream(stream)))
+    return indices
+
+
+def dsa_topk_select(scores: torch.Tensor, ld: int, batch: Batch, k: int, k_per_query: Optional[torch.Tensor] = None,
+                    window: int = 0, indices: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-query k (int32 [T] or None) and the union with the last `window` positions; returns int32
+    [T, k + window], ascending positions then -1."""
+    T = batch.num_queries
+    if indices is None:
+        indices = torch.empty((T, k + window), dtype=torch.int32, device=scores.device)
+    b = batch.struct()
+    _check(load().dsa_topk_select(_ptr(scores), int(ld), ctypes.byref(b), int(k), _ptr(k_per_query), int(window),
+                                  _ptr(indices), None, 0, _stream(stream)))
     return indices
 
 
