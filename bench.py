@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--stage", default="all",
                     choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy", "write_path"],
                     help="profiling aid: run only this stage --steps times (no JSON line)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="selection variant: add the last W positions of each query to its top-k (set union)")
+    ap.add_argument("--dynamic-k", action="store_true",
+                    help="selection variant: a per-query k, drawn uniformly from [k/2, k] (seed 7)")
     ap.add_argument("--write-path", action="store_true",
                     help="measure the cache write path (query rotation + key / latent append) of the workload's "
                          "query tokens instead of the forward; prints its own JSON line")
@@ -74,8 +78,9 @@ def parse():
 # algorithmic work per launch
 
 
-def algorithmic(p, stage):
-    """(bytes, flops) the method must move / compute for one launch of a stage."""
+def algorithmic(p, stage, selected=None):
+    """(bytes, flops) the method must move / compute for one launch of a stage.  selected: the number
+    of selected positions of each query when a selection variant is used (else min(n, k))."""
     s = p.spec
     n = p.q_len.astype(np.int64)
     k = s.topk
@@ -93,6 +98,8 @@ def algorithmic(p, stage):
         flops = int(n[long_].sum()) * HI * 128 * 2
         return kbytes + qbytes + sbytes, flops
     if stage == "topk":
+        if selected is not None:
+            return int(n.sum()) * 4 + int(selected.sum()) * 4, 0
         return int(n[long_].sum()) * 4 + s.T * k * 4, 0
     if stage == "write_path":
         # every query token: its indexer key and latent row appended (sources bf16), its query
@@ -104,7 +111,7 @@ def algorithmic(p, stage):
         queries = 4 + HI * (128 * 2 + 128 * elt + fp8s) + H * 64 * 2 * 2
         return s.T * (append + queries), 0
     if stage == "sparse_mla":
-        cnt = np.minimum(n, k)
+        cnt = np.minimum(n, k) if selected is None else selected.astype(np.int64)
         gather = int(cnt.sum()) * (576 * 2 + 4)
         qo = s.T * H * (576 * 2 + 512 * 2 + 4)
         flops = int(cnt.sum()) * H * (576 + 512) * 2
@@ -172,16 +179,30 @@ def main():
 
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ind = torch.empty((T, k), dtype=torch.int32, device=dev)
+    variant = args.window > 0 or args.dynamic_k
+    width = k + args.window
+    kq = None
+    if args.dynamic_k:
+        kq_np = np.random.default_rng(7).integers(k // 2, k + 1, T).astype(np.int32)
+        kq = torch.from_numpy(kq_np).to(dev)
+    ind = torch.empty((T, width), dtype=torch.int32, device=dev)
     ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_FORWARD, b, k, H)), dtype=torch.uint8, device=dev)
     scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=dev)
-    mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, k, H)
+    mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, width, H)
     mla_ws = torch.empty(max(1, mla_ws_n), dtype=torch.uint8, device=dev)
 
     if args.write_path or args.stage == "write_path":
         return write_path_bench(args, spec, p, dp, dev, stream)
 
     def forward():
+        if variant:
+            # selection variant: the three steps through their own entry points
+            dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, b, spec.idx_scale, scores=scores,
+                                   ld=ld, stream=stream)
+            dsa.dsa_topk_select(scores, ld, b, k, kq, args.window, indices=ind, stream=stream)
+            dsa.dsa_sparse_mla(dp.q_mla, dp.latent, b, ind, spec.softmax_scale, out=out, lse=lse,
+                               workspace=mla_ws if mla_ws_n else None, stream=stream)
+            return
         dsa.dsa_forward(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, k, dp.q_mla, dp.latent, b, spec.softmax_scale,
                         idx_scale=spec.idx_scale, indices_out=ind, out=out, lse=lse, workspace=ws, stream=stream)
 
@@ -190,6 +211,8 @@ def main():
             return lambda: dsa.dsa_indexer_scores(dp.q_idx, dp.q_idx_scale, dp.w, dp.k_cache, b, spec.idx_scale,
                                                    scores=scores, ld=ld, stream=stream)
         if stage == "topk":
+            if variant:
+                return lambda: dsa.dsa_topk_select(scores, ld, b, k, kq, args.window, indices=ind, stream=stream)
             return lambda: dsa.dsa_topk(scores, ld, b, k, indices=ind, stream=stream)
         if stage == "sparse_mla":
             return lambda: dsa.dsa_sparse_mla(dp.q_mla, dp.latent, b, ind, spec.softmax_scale, out=out, lse=lse,
@@ -262,19 +285,20 @@ def main():
 
     # per-stage timing through the separate entry points (same kernels, same launch shapes)
     stages = {}
+    selected = (ind >= 0).sum(dim=1).cpu().numpy() if variant else None
     for st in ("indexer", "topk", "sparse_mla"):
-        if st != "sparse_mla" and p.max_len <= k:
+        if st != "sparse_mla" and p.max_len <= k and not variant:
             continue
         fn = stage_fn(st)
         fn()
         sms, _ = timed(fn, max(5, min(args.steps, 30)))
-        nbytes, flops = algorithmic(p, st)
+        nbytes, flops = algorithmic(p, st, selected)
         stages[st] = {"mean_us": round(float(sms.mean() * 1e3), 3), "alg_bytes": nbytes, "alg_flops": flops}
     forward()   # leave the outputs of a full forward in place
     dom = max(stages, key=lambda s_: stages[s_]["mean_us"])
     d = stages[dom]
     bound, prec = bound_of(p, dom)
-    traffic = recorded_traffic(dom, args.workload)
+    traffic = None if variant else recorded_traffic(dom, args.workload)
     if bound == "hbm":
         achieved = d["alg_bytes"] / (d["mean_us"] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -300,10 +324,21 @@ def main():
         # one pass is short); every repetition is the same, full oracle forward
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.forward(p.q_idx, spec.idx_dtype, p.q_idx_scale, p.w, p.k_idx, spec.idx_dtype, p.k_idx_scale,
-                           p.q_mla, p.latent, p.q_seq, p.q_len, k, seq_stride=p.seq_stride,
-                           page_table=p.page_table, page_size=spec.page_size, scale=spec.idx_scale,
-                           softmax_scale=spec.softmax_scale, qsel=rows, nthreads=threads)
+            if variant:
+                osc = oracle.indexer(p.q_idx, spec.idx_dtype, p.q_idx_scale, p.w, p.k_idx, spec.idx_dtype,
+                                     p.k_idx_scale, p.q_seq, p.q_len, seq_stride=p.seq_stride,
+                                     page_table=p.page_table, page_size=spec.page_size, scale=spec.idx_scale,
+                                     qsel=rows, nthreads=threads)
+                osel = oracle.topk_select(osc, p.q_len[rows], k, None if kq is None else kq_np[rows], args.window,
+                                          nthreads=threads)
+                oracle.sparse_mla(p.q_mla, p.latent, p.q_seq, p.q_len, osel, seq_stride=p.seq_stride,
+                                  page_table=p.page_table, page_size=spec.page_size,
+                                  softmax_scale=spec.softmax_scale, qsel=rows, nthreads=threads)
+            else:
+                oracle.forward(p.q_idx, spec.idx_dtype, p.q_idx_scale, p.w, p.k_idx, spec.idx_dtype, p.k_idx_scale,
+                               p.q_mla, p.latent, p.q_seq, p.q_len, k, seq_stride=p.seq_stride,
+                               page_table=p.page_table, page_size=spec.page_size, scale=spec.idx_scale,
+                               softmax_scale=spec.softmax_scale, qsel=rows, nthreads=threads)
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= 5.0 or reps >= 50:
@@ -325,7 +360,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "query_tokens": T, "sequences": spec.B,
+        "config": {"workload": args.workload + (f"+window{args.window}" if args.window else "")
+                               + ("+dynamic-k" if args.dynamic_k else ""), "query_tokens": T, "sequences": spec.B,
                    "max_context": int(p.max_len), "topk": k, "indexer_heads": spec.idx_heads,
                    "indexer_dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[spec.idx_dtype],
                    "mla_heads": H, "latent": "bf16 576/512", "paged": spec.paged,
