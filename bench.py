@@ -44,7 +44,8 @@ CPU_SAMPLE = {"tiny-prefill-L1024": 1024, "decode-B64-ctx8192": 64, "prefill-L16
               "mtp-decode-B32x2-ctx65536-paged": 24, "ragged-decode-B16-paged": 16}
 
 KERNEL_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "sparse_mla": "sparse_mla.hip",
-                 "write_path": "cache_write.hip"}
+                 "write_path": "cache_write.hip", "value_restore": "value_restore.hip"}
+VALUE_DH = 128   # value width per head used for the value-restore measurement
 
 # Rotated spans used for the write-path measurement: the indexer key's first 64 of 128 dims, and
 # the latent row's decoupled channel (the 64 dims after the 512 latent dims), adjacent pairs, base 1e4.
@@ -62,12 +63,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check before timing")
     ap.add_argument("--stage", default="all",
-                    choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy", "write_path"],
+                    choices=["all", "forward", "indexer", "topk", "sparse_mla", "copy", "write_path",
+                             "value_restore"],
                     help="profiling aid: run only this stage --steps times (no JSON line)")
     ap.add_argument("--window", type=int, default=0,
                     help="selection variant: add the last W positions of each query to its top-k (set union)")
     ap.add_argument("--dynamic-k", action="store_true",
                     help="selection variant: a per-query k, drawn uniformly from [k/2, k] (seed 7)")
+    ap.add_argument("--value-restore", action="store_true",
+                    help="measure the value up-projection after sparse MLA (d_h = 128) on the workload's query "
+                         "tokens instead of the forward; prints its own JSON line")
     ap.add_argument("--write-path", action="store_true",
                     help="measure the cache write path (query rotation + key / latent append) of the workload's "
                          "query tokens instead of the forward; prints its own JSON line")
@@ -193,6 +198,8 @@ def main():
 
     if args.write_path or args.stage == "write_path":
         return write_path_bench(args, spec, p, dp, dev, stream)
+    if args.value_restore or args.stage == "value_restore":
+        return value_restore_bench(args, spec, p, dev, stream)
 
     def forward():
         if variant:
@@ -373,6 +380,78 @@ def main():
         "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
         "spot_check": check,
         "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def value_restore_bench(args, spec, p, dev, stream):
+    """Each head's value up-projection of the latent attention output for the workload's query
+    tokens (o [T, H, 512] -> out [T, H, 128], W [H, 128, 512], synthetic bf16)."""
+    import torch
+    import oracle
+    from sparse_attention_sum_amd import dsa
+
+    T, H, dh = spec.T, spec.mla_heads, VALUE_DH
+    g = torch.Generator(device=dev).manual_seed(99)
+    o = (torch.randn((T, H, 512), generator=g, device=dev) / 24).to(torch.bfloat16)
+    w = (torch.randn((H, dh, 512), generator=g, device=dev) / 22.6).to(torch.bfloat16)
+    out = torch.empty((T, H, dh), dtype=torch.bfloat16, device=dev)
+    step = lambda: dsa.dsa_value_restore(o, w, out=out, stream=stream)
+    flush_buf = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if not args.no_flush:
+            torch.sum(flush_buf, dim=0, keepdim=True, out=flush_out)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    us = float(ms.mean() * 1e3)
+    if args.stage == "value_restore":
+        print(json.dumps({"stage": "value_restore", "workload": args.workload, "mean_us": us}))
+        return
+    nbytes = T * H * 512 * 2 + H * dh * 512 * 2 + T * H * dh * 2
+    flops = 2 * T * H * 512 * dh
+    # arithmetic intensity below the bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B): HBM-bound
+    if flops / nbytes < MFMA_PEAK_TFLOPS["bf16"] / HBM_PEAK_GBS * 1e3:
+        achieved = nbytes / (us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops / (us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS["bf16"],
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS["bf16"], 4)}
+    roofline["traffic"] = recorded_traffic("value_restore", args.workload)
+    roofline["kernel"] = "value_restore"
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = np.unique(np.linspace(0, T - 1, num=min(T, 8)).astype(np.int64))
+        ob = o[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+        wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        threads = min(16, len(os.sched_getaffinity(0)))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.value_restore(ob, wb, nthreads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 5.0 or reps >= 100:
+                break
+        cpu = {"value": round(reps * len(rows) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(rows)} of {T} tokens (evenly spaced), fp64 oracle, {reps} repetition(s) in {dt:.2f} s"}
+    line = {
+        "metric": "value restore tokens/s (per-head up-projection of the latent attention output)",
+        "value": round(T / (us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "heads": H, "latent": 512, "d_h": dh,
+                   "cache_state": "hot" if args.no_flush else "flushed between steps"},
+        "roofline": roofline, "cpu_baseline": cpu, "alg_bytes": nbytes, "alg_flops": flops,
+        "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
     }
     print(json.dumps(line), flush=True)
 

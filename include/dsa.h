@@ -152,6 +152,17 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        const dsa_batch* batch, int32_t* indices_out, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Value restore after sparse MLA in MQA form (page "DeepSeek-V3.2加速技术详解", section 3.1
+ * "MHA版MLA VS MQA版MLA": attention runs on the shared latent vectors and each head's value is
+ * restored only afterwards):
+ *     out[t][h][n] = sum_{k < 512} latent_out[t][h][k] * w_uv[h][n][k],   n < d_h
+ *   latent_out  [num_tokens][n_heads][512] bf16 (the out of dsa_sparse_mla)
+ *   w_uv        [n_heads][d_h][512] bf16: row n of head h holds output dim n's 512 weights
+ *   out         [num_tokens][n_heads][d_h] bf16 (fp32 accumulation, round to nearest even)
+ * d_h is 128, 256, 384 or 512; 1 <= n_heads <= 128; the three pointers are 16-byte aligned. */
+dsa_status dsa_value_restore(const void* latent_out, const void* w_uv, int32_t num_tokens, int32_t n_heads,
+                             int32_t d_h, void* out, hipStream_t stream);
+
 /* ---- cache write path -------------------------------------------------------------------------
  * The step before the three above: page "一文讀懂DeepSeek-V3.2核心技術DSA", "DSA 的四步工作流程",
  * first step (the query and key projections carry rotary position information); page "DeepSeek

@@ -11,6 +11,7 @@ Each function follows the definition cited in ``oracle.c``:
   * ``forward``     the three in sequence; the indexer is skipped where n <= k since the selection
                     then does not depend on it;
   * ``topk_select``  per-query k and the union with a sliding window of recent positions;
+  * ``value_restore`` each head's value up-projection of the latent attention output (MQA form);
   * ``rope_rows``, ``rope_store``, ``cache_append``, ``bf16_encode``, ``e4m3_encode``: the cache
                     write path (rotary embedding in double, one rounding to binary32, then bf16 or
                     per-row-scaled fp8 storage, and the paged / contiguous append).
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
                                      P, P, P, I32, D, P, I64, ctypes.c_int]
         _lib.orc_topk.argtypes = [P, I64, I32, P, P, I32, P, ctypes.c_int]
         _lib.orc_topk_select.argtypes = [P, I64, I32, P, P, I32, P, I32, P, ctypes.c_int]
+        _lib.orc_value_restore.argtypes = [P, P, I32, I32, I32, P, ctypes.c_int]
         _lib.orc_sparse_mla.argtypes = [P, I32, I32, I32, I32, P, I64, P, I32, I32,
                                         P, P, P, I32, P, I32, D, P, P, ctypes.c_int]
         _lib.orc_bf16_encode.argtypes = [ctypes.c_float]
@@ -250,3 +252,14 @@ def cache_append(x, src_dtype: str, seq, pos, num_seqs: int, rope, cache, cache_
                            cache.shape[0], int(seq_stride), _ptr(pt), 0 if pt is None else pt.shape[1],
                            int(page_size))
     return cache
+
+
+def value_restore(o, w, nthreads=0):
+    """o: bf16 bits [T, H, 512]; w: bf16 bits [H, dh, 512].  Returns out [T, H, dh] float64 with
+    out[t, h, n] = sum_k o[t, h, k] * w[h, n, k]."""
+    o = _c(o, np.uint16); w = _c(w, np.uint16)
+    T, H, _ = o.shape
+    dh = w.shape[1]
+    out = np.empty((T, H, dh), dtype=np.float64)
+    lib().orc_value_restore(_ptr(o), _ptr(w), T, H, dh, _ptr(out), int(nthreads))
+    return out

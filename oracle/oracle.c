@@ -522,3 +522,34 @@ int orc_cache_append(const void* x, int src_dtype, int32_t T, int width, const i
     free(row); free(v);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* 5. value restore after sparse MLA in MQA form                                              */
+/* Page "DeepSeek-V3.2加速技术详解", section 3.1 "MHA版MLA VS MQA版MLA": attention runs on the
+   latent vectors and each head's value is restored afterwards:
+       out[t][h][n] = sum_{k < 512} o[t][h][k] * W[h][n][k]      (n < dh)
+   o: bf16 [T][H][512]; W: bf16 [H][dh][512]; out: doubles [T][H][dh]. */
+typedef struct { const uint16_t* o; const uint16_t* w; int32_t H, dh; double* out; } vr_ctx;
+
+static void vr_one(void* p, int64_t t) {
+    vr_ctx* c = (vr_ctx*)p;
+    double* ov = (double*)malloc(sizeof(double) * 512);
+    for (int32_t h = 0; h < c->H; h++) {
+        for (int k = 0; k < 512; k++) ov[k] = orc_bf16_value(c->o[(t * c->H + h) * 512 + k]);
+        for (int32_t n = 0; n < c->dh; n++) {
+            const uint16_t* wr = c->w + ((int64_t)h * c->dh + n) * 512;
+            double s = 0.0;
+            for (int k = 0; k < 512; k++) s += ov[k] * orc_bf16_value(wr[k]);
+            c->out[(t * c->H + h) * (int64_t)c->dh + n] = s;
+        }
+    }
+    free(ov);
+}
+
+int orc_value_restore(const uint16_t* o, const uint16_t* w, int32_t T, int32_t H, int32_t dh, double* out,
+                      int nthreads) {
+    vr_ctx c;
+    c.o = o; c.w = w; c.H = H; c.dh = dh; c.out = out;
+    orc_parallel(vr_one, &c, T, nthreads);
+    return 0;
+}

@@ -359,4 +359,19 @@ dsa_status dsa_rope_queries(const void* q_idx_in, int32_t q_idx_in_dtype, int32_
                       "rope_queries launch");
 }
 
+dsa_status dsa_value_restore(const void* latent_out, const void* w_uv, int32_t num_tokens, int32_t n_heads,
+                             int32_t d_h, void* out, hipStream_t stream) {
+    if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "value_restore: num_tokens < 0");
+    if (n_heads < 1 || n_heads > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "value_restore: n_heads %d not in [1,128]", n_heads);
+    if (d_h < 128 || d_h > 512 || d_h % 128 != 0)
+        return fail(DSA_ERR_UNSUPPORTED, "value_restore: d_h %d must be 128, 256, 384 or 512", d_h);
+    if (num_tokens == 0) return DSA_OK;
+    if (!latent_out || !w_uv || !out) return fail(DSA_ERR_INVALID_ARG, "value_restore: a pointer is NULL");
+    if (((uintptr_t)latent_out | (uintptr_t)w_uv | (uintptr_t)out) & 15)
+        return fail(DSA_ERR_INVALID_ARG, "value_restore: pointers must be 16-byte aligned");
+    return hip_status(dsa::launch_value_restore((const uint16_t*)latent_out, (const uint16_t*)w_uv, num_tokens, n_heads,
+                                                d_h, (uint16_t*)out, stream),
+                      "value_restore launch");
+}
+
 }  // extern "C"

@@ -48,4 +48,8 @@ hipError_t launch_rope_queries(const void* qi_in, int qi_dtype, int Hi, void* qi
                                const RopeView& ri, uint16_t* qm, int Hm, const RopeView& rm, const int32_t* pos,
                                int T, hipStream_t st);
 
+// Value restore after sparse MLA (MQA form): out[t][h][:dh] = o[t][h][:512] . W[h]^T, W [H][dh][512].
+hipError_t launch_value_restore(const uint16_t* o, const uint16_t* w, int T, int H, int dh, uint16_t* out,
+                                hipStream_t st);
+
 }  // namespace dsa

@@ -24,7 +24,7 @@ DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_workspace_size",
            "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries",
-           "dsa_topk_select")
+           "dsa_topk_select", "dsa_value_restore")
 
 
 class DsaError(RuntimeError):
@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
     L.dsa_indexer_scores.argtypes = [P, I32, P, P, I32, I32, CP, BP, F, P, I64, P]
     L.dsa_topk.argtypes = [P, I64, BP, I32, P, P, ctypes.c_size_t, P]
     L.dsa_topk_select.argtypes = [P, I64, BP, I32, P, I32, P, P, ctypes.c_size_t, P]
+    L.dsa_value_restore.argtypes = [P, P, I32, I32, I32, P, P]
     L.dsa_sparse_mla.argtypes = [P, I32, I32, I32, CP, BP, P, I32, F, P, P, P, ctypes.c_size_t, P]
     L.dsa_forward.argtypes = [P, I32, P, P, I32, CP, F, I32, P, I32, CP, F, BP, P, P, P, P, ctypes.c_size_t, P]
     L.dsa_workspace_size.argtypes = [I32, BP, I32, I32, I32]
@@ -96,7 +97,7 @@ def load() -> ctypes.CDLL:
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_cache_append",
-                 "dsa_rope_queries", "dsa_topk_select"):
+                 "dsa_rope_queries", "dsa_topk_select", "dsa_value_restore"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -282,3 +283,15 @@ def dsa_rope_queries(q_idx_in: Optional[torch.Tensor], q_idx_out: Optional[torch
                                    None if ir is None else ctypes.byref(ir), _ptr(q_mla),
                                    0 if q_mla is None else int(q_mla.shape[1]),
                                    None if mr is None else ctypes.byref(mr), _ptr(pos), T, _stream(stream)))
+
+
+def dsa_value_restore(latent_out: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """latent_out [T, H, 512] bf16, w_uv [H, d_h, 512] bf16 -> out [T, H, d_h] bf16 (each head's value
+    up-projection of the latent attention output)."""
+    T, H, _ = latent_out.shape
+    dh = int(w_uv.shape[1])
+    if out is None:
+        out = torch.empty((T, H, dh), dtype=torch.bfloat16, device=latent_out.device)
+    _check(load().dsa_value_restore(_ptr(latent_out), _ptr(w_uv), T, H, dh, _ptr(out), _stream(stream)))
+    return out

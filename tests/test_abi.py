@@ -186,3 +186,24 @@ def test_rope_queries_validation(lib):
     assert _ropeq(lib, ri=dsa._Rope(-2, 64, 1, 10000.0)) == dsa.DSA_ERR_INVALID_ARG
     # nothing to do: no indexer queries and an MLA rotation of width 0
     assert _ropeq(lib, qi=None, rm=dsa._Rope(0, 0, 1, 10000.0)) == dsa.DSA_OK
+
+
+def test_value_restore_validation(lib):
+    assert lib.dsa_value_restore(FAKE, FAKE, -1, 128, 128, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_value_restore(FAKE, FAKE, 4, 0, 128, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_value_restore(FAKE, FAKE, 4, 129, 128, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_value_restore(FAKE, FAKE, 4, 128, 64, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED     # d_h % 128
+    assert lib.dsa_value_restore(FAKE, FAKE, 4, 128, 640, FAKE, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_value_restore(None, FAKE, 4, 128, 128, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_value_restore(FAKE + 2, FAKE, 4, 128, 128, FAKE, None) == dsa.DSA_ERR_INVALID_ARG   # alignment
+    assert b"aligned" in lib.dsa_last_error()
+    assert lib.dsa_value_restore(None, None, 0, 128, 128, None, None) == dsa.DSA_OK                   # nothing to do
+
+
+def test_topk_select_validation(lib):
+    b = _batch()
+    assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 0, None, 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 16, None, -1, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 65000, None, 1000, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_select(FAKE, 99, ctypes.byref(b), 16, None, 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 16, None, 0, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
