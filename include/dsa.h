@@ -110,7 +110,10 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
  *   scores   [T][ld] floats; only entries s < n_t of row t are read
  *   indices  [T][k] int32: the selected positions in ascending order, then -1 padding (n_t < k)
  * Scores are compared as real numbers (+0 == -0); equal scores go to the lower position.  NaN scores
- * are not supported.  workspace may be NULL (this operation needs none). */
+ * are not supported.  workspace may be NULL: then each row is selected by one workgroup.  With a
+ * workspace of dsa_workspace_size(DSA_OP_TOPK, ...) bytes (non-zero for rows longer than 65536),
+ * long rows go through two passes -- slices of the row each keep their best k (key, position)
+ * candidates, then one workgroup per row selects from those -- with the same result. */
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -123,8 +126,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int
  *   window       W >= 0: the W most recent positions n_t - W .. n_t - 1 join the selection (set union)
  *   indices      [T][k + window] int32: the union in ascending order, then -1 padding; it feeds
  *                dsa_sparse_mla with k + window as its k
- * 1 <= k and k + window <= 65536.  With k_per_query NULL and window 0 this is dsa_topk.  workspace
- * may be NULL. */
+ * 1 <= k and k + window <= 65536.  With k_per_query NULL and window 0 this is dsa_topk.  The
+ * workspace is used as in dsa_topk (NULL allowed). */
 dsa_status dsa_topk_select(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k,
                            const int32_t* k_per_query, int32_t window, int32_t* indices, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);

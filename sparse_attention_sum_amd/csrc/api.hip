@@ -2,6 +2,7 @@
 //
 // Every entry point validates its arguments on the host and returns before launching anything when
 // they are wrong.  Kernels are enqueued on the caller's stream; nothing here waits for the device.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -181,8 +182,9 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* batch, int32_t k, int32_t
     const int T = batch->num_queries;
     switch (op) {
         case DSA_OP_INDEXER:
-        case DSA_OP_TOPK:
             return 0;
+        case DSA_OP_TOPK:
+            return k > 0 ? dsa::topk_workspace_bytes(view(batch), k) : 0;
         case DSA_OP_SPARSE_MLA:
             return k > 0 ? dsa::mla_workspace_bytes(T, k, n_heads) : 0;
         case DSA_OP_FORWARD: {
@@ -190,7 +192,9 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* batch, int32_t k, int32_t
             size_t bytes = 0;
             if (batch->max_len > k) bytes += align256((size_t)T * score_ld(batch) * sizeof(float));
             bytes += align256((size_t)T * k * sizeof(int32_t));
-            bytes += dsa::mla_workspace_bytes(T, k, n_heads);
+            // the top-k candidates and the MLA partials share one region (used one after the other)
+            bytes += std::max(align256(dsa::mla_workspace_bytes(T, k, n_heads)),
+                              align256(dsa::topk_workspace_bytes(view(batch), k)));
             return bytes;
         }
     }
@@ -211,22 +215,19 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
 
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     dsa_status s = check_batch(batch);
     if (s != DSA_OK) return s;
     if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
     if (batch->num_queries > 0 && (!indices || (!scores && batch->max_len > k)))
         return fail(DSA_ERR_INVALID_ARG, "topk: scores or indices is NULL");
     if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "topk: ld %lld < max_len %d", (long long)ld, batch->max_len);
-    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, nullptr, 0, indices, stream), "topk launch");
+    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, nullptr, 0, indices, workspace, workspace_bytes, stream),
+                      "topk launch");
 }
 
 dsa_status dsa_topk_select(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k,
                            const int32_t* k_per_query, int32_t window, int32_t* indices, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     dsa_status s = check_batch(batch);
     if (s != DSA_OK) return s;
     if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
@@ -236,7 +237,8 @@ dsa_status dsa_topk_select(const float* scores, int64_t ld, const dsa_batch* bat
         return fail(DSA_ERR_INVALID_ARG, "topk_select: scores or indices is NULL");
     if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "topk_select: ld %lld < max_len %d", (long long)ld, batch->max_len);
     if (batch->num_queries == 0) return DSA_OK;
-    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, k_per_query, window, indices, stream),
+    return hip_status(dsa::launch_topk(scores, ld, view(batch), k, k_per_query, window, indices, workspace,
+                                       workspace_bytes, stream),
                       "topk_select launch");
 }
 
@@ -273,13 +275,16 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
     const size_t score_bytes = need_scores ? align256((size_t)T * ld * sizeof(float)) : 0;
     const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
     const size_t mla_bytes = dsa::mla_workspace_bytes(T, k, n_heads);
-    need = score_bytes + idx_bytes + mla_bytes;
+    const size_t topk_bytes = dsa::topk_workspace_bytes(view(batch), k);
+    const size_t shared_bytes = std::max(align256(mla_bytes), align256(topk_bytes));   // top-k, then MLA
+    need = score_bytes + idx_bytes + shared_bytes;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     uint8_t* ws = (uint8_t*)workspace;
     float* scores = need_scores ? (float*)ws : nullptr;
     int32_t* idx = indices_out ? indices_out : (int32_t*)(ws + score_bytes);
     void* mla_ws = mla_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
+    void* topk_ws = topk_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
 
     const dsa::BatchView bv = view(batch);
     if (need_scores) {
@@ -288,7 +293,8 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        "forward: indexer launch");
         if (s != DSA_OK) return s;
     }
-    s = hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, idx, stream), "forward: topk launch");
+    s = hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, idx, topk_ws, topk_bytes, stream),
+                   "forward: topk launch");
     if (s != DSA_OK) return s;
     return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
                                              (uint16_t*)out, lse, mla_ws, stream),

@@ -20,8 +20,11 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
 
 // Top-k per query row (ascending positions, -1 padded), rows of k + window entries: query t's best
 // clamp(kq[t], 0, k) positions (k when kq is null) united with its last `window` positions.
+// A workspace of topk_workspace_bytes() (0 when not useful) lets long rows go through two passes
+// (slices of the row, then a merge of their candidates); without it, one workgroup per row.
+size_t topk_workspace_bytes(const BatchView& bv, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, const int32_t* kq, int window,
-                       int32_t* idx, hipStream_t st);
+                       int32_t* idx, void* ws, size_t ws_bytes, hipStream_t st);
 
 // Sparse MLA.  `splits` partitions the k index slots; partial results go to the workspace when
 // splits > 1.  mla_splits() is the split count the library uses for a batch.

@@ -35,6 +35,7 @@ constexpr int kDigitBits = 11; // radix digit width
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 2;
 constexpr int kGatherKeys = 16;  // consecutive keys per thread per step of the candidate gather
+constexpr int kTwoPassMin = 65536;   // rows longer than this go through two passes (given a workspace)
 
 enum { kModeCached = 0, kModeGlobal = 1, kModeCand = 2 };
 
@@ -162,10 +163,9 @@ __device__ __forceinline__ uint32_t wave_reduce_min(uint32_t v) {
 // inclusive DPP scan over the lanes' packed (above, equal) counts gives every lane the output slot
 // of its first take -- equal entries are taken in entry order while the running count of earlier
 // equal entries is below need_eq.
-template <typename Key4, typename Pos4>
+template <typename Key4, typename Pos4, typename Emit>
 __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32_t mask, uint32_t thr,
-                                        uint32_t need_eq, int k, int32_t* __restrict__ orow,
-                                        uint32_t (&wcnt)[2][kTkWaves], int wlo, uint32_t* first_win) {
+                                        uint32_t need_eq, int k, uint32_t (&wcnt)[2][kTkWaves], Emit&& emit) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = (((nw + kTkWaves - 1) / kTkWaves) + 255) & ~255;
     const int beg = min(nw, wave * seg), end = min(nw, beg + seg);
@@ -194,6 +194,7 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
         const uint4 kk = key4(i0, end);
         const int4 pp = pos4(i0);
         const uint32_t v[4] = {kk.x & mask, kk.y & mask, kk.z & mask, kk.w & mask};
+        const uint32_t raw[4] = {kk.x, kk.y, kk.z, kk.w};
         const int p[4] = {pp.x, pp.y, pp.z, pp.w};
         uint32_t g = 0, e = 0;
 #pragma unroll
@@ -217,12 +218,7 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
                 eq_seen++;
             }
             if (take) {
-                if (at < (uint32_t)k) {
-                    // positions in the window [wlo, n) are written with the window block; the
-                    // first of them marks where that block starts
-                    if (p[j] < wlo) orow[at] = p[j];
-                    else atomicMin(first_win, at);
-                }
+                if (at < (uint32_t)k) emit(at, p[j], raw[j]);
                 at++;
             }
         }
@@ -232,12 +228,27 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
     }
 }
 
+// Long rows in two passes (workspace): slice s of row t (positions [s * len, (s + 1) * len)) keeps
+// its own best kt entries as (key, position) candidates -- the row's best kt are among the union of
+// the slices' best kt under the same order -- and one workgroup per row then selects from at most
+// nslices * kt candidates, which it holds in LDS in position order.
+struct TkSlices {
+    uint32_t* ckey;      // [T][nslices][k] candidate keys
+    int32_t* cpos;       // [T][nslices][k] candidate positions
+    int32_t* ccnt;       // [T][nslices] candidates per slice
+    int nslices, slice_len;
+};
+
 // Query t selects its best kt = clamp(kq[t], 0, k) positions (k when kq is null; all when n <= kt)
 // and adds its last `window` positions; the union is written in ascending order to a row of
 // `width` = k + window entries, -1 padded.  The plain top-k is kq = null, window = 0.
+// PASS 0: the whole row in one workgroup; PASS 1: one slice of a row -> candidates; PASS 2: the
+// selection from a row's candidates.
+template <int PASS>
 __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict__ scores, int64_t ld,
                                                         BatchView bv, int k, const int32_t* __restrict__ kq,
-                                                        int window, int width, int32_t* __restrict__ out) {
+                                                        int window, int width, int32_t* __restrict__ out,
+                                                        TkSlices sl) {
     // cached rows: keys[kCap]; long rows: candidate keys [0, kCandCap) + positions [kCandCap, kCap)
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ uint32_t hist[kHistCopies][kBins];   // copies shared by alternate waves (fewer collisions)
@@ -252,27 +263,83 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     const int n = max(0, min(bv.q_len[t], bv.max_len));
     const int kt = kq != nullptr ? max(0, min(kq[t], k)) : k;
     const int wn = min(window, n), wlo = n - wn;   // the window: positions [wlo, n)
-    if (n <= kt) {
-        for (int i = tid; i < width; i += kTkBlock) orow[i] = i < n ? i : -1;
+    if (n <= kt) {   // (pass 1 writes nothing: pass 2 takes the same exit)
+        if (PASS != 1)
+            for (int i = tid; i < width; i += kTkBlock) orow[i] = i < n ? i : -1;
         return;
     }
     if (kt == 0) {
-        for (int i = tid; i < width; i += kTkBlock) orow[i] = i < wn ? wlo + i : -1;
+        if (PASS != 1)
+            for (int i = tid; i < width; i += kTkBlock) orow[i] = i < wn ? wlo + i : -1;
         return;
     }
-    const float* srow = scores + (int64_t)t * ld;
+    // pass 1: this workgroup's slice [s0, s0 + nrow) of the row
+    const int slice = PASS == 1 ? (int)blockIdx.y : 0;
+    const int s0 = PASS == 1 ? slice * sl.slice_len : 0;
+    const int nrow = PASS == 1 ? min(sl.slice_len, n - s0) : n;
+    const int64_t cbase = ((int64_t)t * sl.nslices + slice) * k;   // pass 1: this slice's candidate slots
+    const int kts = PASS == 1 ? min(kt, nrow) : kt;                // pass 1: the slice keeps its best kts
+    const float* srow = scores + (int64_t)t * ld + s0;
+    if (PASS == 1) {
+        if (nrow <= kts) {   // a slice no longer than kt: every entry is a candidate (nrow <= 0: none)
+            for (int i = tid; i < nrow; i += kTkBlock) {
+                sl.ckey[cbase + i] = order_key(srow[i]);
+                sl.cpos[cbase + i] = s0 + i;
+            }
+            if (tid == 0) sl.ccnt[(int64_t)t * sl.nslices + slice] = max(nrow, 0);
+            return;
+        }
+    }
     uint32_t* keys = lds;
     int32_t* cpos = (int32_t*)(lds + kCandCap);
-    int mode = n <= kCap ? kModeCached : kModeGlobal;
-    int nw = n;   // size of the working set
+    int mode = PASS == 2 ? kModeCand : nrow <= kCap ? kModeCached : kModeGlobal;
+    int nw = nrow;   // size of the working set
 
     // keys (cached in LDS when the row fits) and their min / max; the row is read with 16-byte loads,
     // kUnroll of them in flight per thread, when it is 16-byte aligned
     const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    if (mode == kModeCached) {
+    if (PASS == 2) {
+        // the row's candidates, slice after slice (each in position order), into LDS
+        __shared__ int coff[kTkWaves + 1];
+        if (tid == 0) {
+            int acc = 0;
+            for (int sI = 0; sI < sl.nslices; sI++) {
+                coff[sI] = acc;
+                acc += sl.ccnt[(int64_t)t * sl.nslices + sI];
+            }
+            coff[sl.nslices] = acc;
+        }
+        __syncthreads();
+        nw = coff[sl.nslices];
+        // entry i of the row's candidate list is entry i - coff[s] of slice s (coff[s] <= i <
+        // coff[s + 1]); every load is independent, kUnroll of them per thread per step
+        for (int i0 = tid; i0 < nw; i0 += kTkBlock * kUnroll) {
+            uint32_t kk[kUnroll];
+            int32_t pp[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++) {
+                const int i = min(i0 + u * kTkBlock, nw - 1);
+                int sI = 0;
+                while (sI + 1 < sl.nslices && coff[sI + 1] <= i) sI++;
+                const int64_t src = ((int64_t)t * sl.nslices + sI) * k + (i - coff[sI]);
+                kk[u] = sl.ckey[src];
+                pp[u] = sl.cpos[src];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++) {
+                const int i = i0 + u * kTkBlock;
+                if (i < nw) {
+                    keys[i] = kk[u];
+                    cpos[i] = pp[u];
+                    lo = min(lo, kk[u]);
+                    hi = max(hi, kk[u]);
+                }
+            }
+        }
+    } else if (mode == kModeCached) {
         for_each_raw4<kUnroll>(
-            srow, n, vec,
+            srow, nrow, vec,
             [&](int i, const uint4& kk) {
                 *(uint4*)(keys + i) = kk;
                 lo = min(lo, min(min(kk.x, kk.y), min(kk.z, kk.w)));
@@ -285,7 +352,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
             });
     } else {
         for_each_raw4<kUnrollLong>(
-            srow, n, vec,
+            srow, nrow, vec,
             [&](int, const uint4& kk) {
                 lo = min(lo, min(min(kk.x, kk.y), min(kk.z, kk.w)));
                 hi = max(hi, max(max(kk.x, kk.y), max(kk.z, kk.w)));
@@ -319,7 +386,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
 
     uint32_t prefix = lo;            // bits resolved so far (under `mask`)
     uint32_t mask = 0xffffffffu;
-    uint32_t remaining = (uint32_t)kt; // keys still to take among those matching the prefix
+    uint32_t remaining = (uint32_t)kts; // keys still to take among those matching the prefix
 
     // Ordered gather of the candidates (keys with (key & mask) >= prefix) of a long row into LDS:
     // thread t takes keys [base + 16 t, +16) of each step, a block-wide prefix sum gives their
@@ -329,15 +396,15 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
         uint32_t total = 0;
         constexpr int kStep = kTkBlock * kGatherKeys;
         float cur[kGatherKeys], nxt[kGatherKeys];
-        load_run(srow, n, vec, kGatherKeys * tid, cur);
-        for (int base = 0; base < n; base += kStep) {
+        load_run(srow, nrow, vec, kGatherKeys * tid, cur);
+        for (int base = 0; base < nrow; base += kStep) {
             const int i0 = base + kGatherKeys * tid;
-            if (base + kStep < n) load_run(srow, n, vec, i0 + kStep, nxt);
+            if (base + kStep < nrow) load_run(srow, nrow, vec, i0 + kStep, nxt);
             uint32_t kk[kGatherKeys], c = 0;
 #pragma unroll
             for (int j = 0; j < kGatherKeys; j++) {
                 kk[j] = order_key(cur[j]);
-                c += (i0 + j < n && (kk[j] & mask) >= prefix) ? 1u : 0u;
+                c += (i0 + j < nrow && (kk[j] & mask) >= prefix) ? 1u : 0u;
             }
             const uint32_t incl = wave_incl_scan(c);   // inclusive prefix over the wave's lanes
             if (lane == 63) red[0][wave] = incl;
@@ -350,7 +417,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
             }
 #pragma unroll
             for (int j = 0; j < kGatherKeys; j++) {
-                if (i0 + j < n && (kk[j] & mask) >= prefix) {
+                if (i0 + j < nrow && (kk[j] & mask) >= prefix) {
                     if (at < (uint32_t)kCandCap) {
                         lds[at] = kk[j];
                         cpos[at] = i0 + j;
@@ -435,8 +502,21 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     // exit, where the bin holds exactly `remaining` keys).  (All keys equal: the first k.)
     const uint32_t thr = prefix, need_eq = remaining;
 
+    if (PASS == 1) {   // the slice's best kts as candidates, in position order
+        compact(key4, pos4, nw, mask, thr, need_eq, kts, wcnt, [&](uint32_t at, int pos, uint32_t key) {
+            sl.ckey[cbase + at] = key;
+            sl.cpos[cbase + at] = s0 + pos;
+        });
+        if (tid == 0) sl.ccnt[(int64_t)t * sl.nslices + slice] = kts;
+        return;
+    }
     if (tid == 0) first_win = (uint32_t)kt;   // ordered before compact's writes by its barrier
-    compact(key4, pos4, nw, mask, thr, need_eq, kt, orow, wcnt, wlo, &first_win);
+    // positions in the window [wlo, n) are written with the window block; the first of them marks
+    // where that block starts
+    compact(key4, pos4, nw, mask, thr, need_eq, kt, wcnt, [&](uint32_t at, int pos, uint32_t) {
+        if (pos < wlo) orow[at] = pos;
+        else atomicMin(&first_win, at);
+    });
     if (wn > 0 || width > kt) {
         // the selected positions below the window fill slots [0, c); then the window, then padding
         __syncthreads();
@@ -447,22 +527,66 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
 
 }  // namespace
 
+// Two passes when a workspace is given and the rows are long: up to 8 slices per row (the merge
+// keeps nslices * k candidates in LDS), each slice short enough to be cached in LDS.
+static bool topk_two_pass(const BatchView& bv, int k, int& nslices, int& slice_len) {
+    if (bv.max_len <= kTwoPassMin || k <= 0) return false;
+    // as few slices as the LDS key cache allows (a slice workgroup holds up to kCap keys, one per
+    // CU): more slices mean more rounds of workgroups and a longer merge
+    nslices = min(min(kTkWaves, kCandCap / k), max(2, (bv.max_len + kCap - 1) / kCap));
+    if (nslices < 2) return false;
+    slice_len = ((bv.max_len + nslices - 1) / nslices + 3) & ~3;
+    return slice_len <= kCap;
+}
+
+size_t topk_workspace_bytes(const BatchView& bv, int k) {
+    int ns = 0, len = 0;
+    if (bv.T <= 0 || !topk_two_pass(bv, k, ns, len)) return 0;
+    const size_t slots = (size_t)bv.T * ns * k;
+    return ((slots * 4 + 255) & ~(size_t)255) * 2 + (size_t)bv.T * ns * 4;
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, const int32_t* kq, int window,
-                       int32_t* idx, hipStream_t st) {
+                       int32_t* idx, void* ws, size_t ws_bytes, hipStream_t st) {
     if (bv.T == 0) return hipSuccess;
+    int ns = 0, len = 0;
+    const size_t need = topk_workspace_bytes(bv, k);
+    if (ws != nullptr && need > 0 && ws_bytes >= need && topk_two_pass(bv, k, ns, len)) {
+        TkSlices sl;
+        const size_t slots = (size_t)bv.T * ns * k;
+        const size_t half = (slots * 4 + 255) & ~(size_t)255;
+        sl.ckey = (uint32_t*)ws;
+        sl.cpos = (int32_t*)((uint8_t*)ws + half);
+        sl.ccnt = (int32_t*)((uint8_t*)ws + 2 * half);
+        sl.nslices = ns;
+        sl.slice_len = len;
+        const size_t shm1 = (size_t)min(len, kCap) * sizeof(uint32_t);
+        const size_t shm2 = (size_t)kLdsWords * sizeof(uint32_t);
+        hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)shm1);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)topk_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm2);
+        if (e != hipSuccess) return e;
+        topk_kernel<1><<<dim3(bv.T, ns), kTkBlock, shm1, st>>>(scores, ld, bv, k, kq, window, k + window, idx, sl);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        topk_kernel<2><<<bv.T, kTkBlock, shm2, st>>>(scores, ld, bv, k, kq, window, k + window, idx, sl);
+        return hipGetLastError();
+    }
     // LDS for the longest row: its keys (rounded up so whole 16-byte reads stay inside), or the
     // candidate area when rows may exceed the key cache
-    size_t words = 0;
     // (with a per-query k any query may select, so the key cache is sized for every row)
+    size_t words = 0;
     if (bv.max_len > (kq != nullptr ? 0 : k))
         words = bv.max_len > kCap ? (size_t)kLdsWords : (size_t)((bv.max_len + 3) & ~3);
     const size_t shm = words * sizeof(uint32_t);
     if (shm > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)shm);
         if (e != hipSuccess) return e;
     }
-    topk_kernel<<<bv.T, kTkBlock, shm, st>>>(scores, ld, bv, k, kq, window, k + window, idx);
+    TkSlices none{};
+    topk_kernel<0><<<bv.T, kTkBlock, shm, st>>>(scores, ld, bv, k, kq, window, k + window, idx, none);
     return hipGetLastError();
 }
 

@@ -189,26 +189,38 @@ def dsa_indexer_scores(q: torch.Tensor, q_scale: Optional[torch.Tensor], weights
     return scores
 
 
+def _topk_workspace(batch: Batch, k: int, workspace, device):
+    """A workspace for the two-pass path of long rows (None when the call needs none)."""
+    if workspace is not None:
+        return workspace
+    need = dsa_workspace_size(DSA_OP_TOPK, batch, k, 1)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+
+
 def dsa_topk(scores: Optional[torch.Tensor], ld: int, batch: Batch, k: int, indices: Optional[torch.Tensor] = None,
-             stream=None) -> torch.Tensor:
+             stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Returns indices [T, k] int32: selected positions ascending, then -1."""
     if indices is None:
         indices = torch.empty((batch.num_queries, k), dtype=torch.int32, device=batch.q_len.device)
+    ws = _topk_workspace(batch, k, workspace, batch.q_len.device)
     b = batch.struct()
-    _check(load().dsa_topk(_ptr(scores), int(ld), ctypes.byref(b), int(k), _ptr(indices), None, 0, _stream(stream)))
+    _check(load().dsa_topk(_ptr(scores), int(ld), ctypes.byref(b), int(k), _ptr(indices), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)))
     return indices
 
 
 def dsa_topk_select(scores: torch.Tensor, ld: int, batch: Batch, k: int, k_per_query: Optional[torch.Tensor] = None,
-                    window: int = 0, indices: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                    window: int = 0, indices: Optional[torch.Tensor] = None, stream=None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-query k (int32 [T] or None) and the union with the last `window` positions; returns int32
     [T, k + window], ascending positions then -1."""
     T = batch.num_queries
     if indices is None:
         indices = torch.empty((T, k + window), dtype=torch.int32, device=scores.device)
+    ws = _topk_workspace(batch, k, workspace, scores.device)
     b = batch.struct()
     _check(load().dsa_topk_select(_ptr(scores), int(ld), ctypes.byref(b), int(k), _ptr(k_per_query), int(window),
-                                  _ptr(indices), None, 0, _stream(stream)))
+                                  _ptr(indices), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return indices
 
 

@@ -6,6 +6,8 @@ sides make on the same values; ties to the lower position).  Rows cover short co
 k_t = 0 (window only), clamped k_t, heavy ties, and rows longer than the LDS key cache (the
 candidate path).  The selection then feeds dsa_sparse_mla with k + window index slots.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -99,3 +101,37 @@ def test_window_selection_feeds_sparse_mla():
                                      softmax_scale=spec.softmax_scale, qsel=rows, nthreads=8)
     check_mla(out[torch.from_numpy(rows).long().cuda()].float().cpu().numpy(),
               lse[torch.from_numpy(rows).long().cuda()].cpu().numpy(), o_ref, l_ref, "window selection")
+
+
+@pytest.mark.parametrize("max_len,k", [(131072, 2048), (100000, 2048), (70000, 1024), (80000, 4096)])
+def test_two_pass_equals_one_pass(max_len, k):
+    """Long rows with a workspace go through slices and a merge; the result must equal the one-pass
+    selection bit for bit (ties, +-0, ragged lengths, per-query k and a window)."""
+    rng = np.random.default_rng(max_len + k)
+    T = 24
+    q_len = rng.integers(k // 2, max_len + 1, T).astype(np.int32)
+    q_len[0] = max_len
+    ld = (max_len + 63) // 64 * 64
+    sc = np.round(rng.normal(0, 1, (T, ld)) * 8) / 8
+    sc[1, ::3] = -0.0
+    sct = torch.from_numpy(sc.astype(np.float32)).cuda()
+    b = _batch(q_len, max_len)
+    log(f"case: two-pass top-k max_len={max_len} k={k}")
+    need = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, b, k, 1)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for kq, W in ((None, 0), (torch.from_numpy(rng.integers(0, k + 1, T).astype(np.int32)).cuda(), 100)):
+        one = torch.empty((T, k + W), dtype=torch.int32, device="cuda")
+        two = torch.empty((T, k + W), dtype=torch.int32, device="cuda")
+        bs = b.struct()
+        L = dsa.load()
+        assert L.dsa_topk_select(sct.data_ptr(), ld, ctypes.byref(bs), k, None if kq is None else kq.data_ptr(), W,
+                                 one.data_ptr(), None, 0, None) == 0
+        assert L.dsa_topk_select(sct.data_ptr(), ld, ctypes.byref(bs), k, None if kq is None else kq.data_ptr(), W,
+                                 two.data_ptr(), ws.data_ptr(), need, None) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), f"kq={kq is not None} W={W}"
+    ref = oracle.topk(sc[:3], q_len[:3], k)
+    got = dsa.dsa_topk(sct, ld, b, k, workspace=ws).cpu().numpy()[:3]
+    for r in range(3):
+        assert sorted(v for v in ref[r] if v >= 0) == [v for v in got[r] if v >= 0]
