@@ -397,14 +397,19 @@ __device__ __forceinline__ void pf_dma(const uint8_t* src, uint32_t lds) {
 __device__ __forceinline__ void pf_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // acc = q_slice . k_subtile^T (32 heads x 32 keys), eight MFMAs; meanwhile the epilogue of the
-// previous chain folds 16 head rows of `prev` into `sum` (w * max(0, x), two VALU per element).
-template <bool EPI>
+// previous chain folds 16 head rows of `prev` into `sum` (w * max(0, x), two VALU per element), and
+// pre(ks) may issue an operand read for a later chain.  Each MFMA is issued before the VALU of its
+// step, so the new accumulator and `prev` are live together and never share registers (shared
+// registers made the next chain's first MFMA wait for the previous chain to drain).
+template <bool EPI, typename Pre>
 __device__ __forceinline__ f32x16 pf_chain(const bf16x8 (&qs)[8], const bf16x8 (&kf)[8], const f32x16& prev,
-                                           const float (&wp)[16], float& sum) {
+                                           const float (&wp)[16], float& sum, Pre&& pre) {
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qs[ks], kf[ks], acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        pre(ks);
         if (EPI) {
             sum = fmaf(wp[2 * ks], relu_bits(prev[2 * ks]), sum);
             sum = fmaf(wp[2 * ks + 1], relu_bits(prev[2 * ks + 1]), sum);
@@ -480,6 +485,9 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
         }
     }
     if (paged) __syncthreads();   // the page table above
+    // scalar loads still outstanding in the loop would force every LDS wait there to wait for all
+    // (scalar loads return out of order): have the ones the loop uses land before this wait
+    asm volatile("" ::"s"(scale), "s"(ld), "s"(scores));
     __builtin_amdgcn_s_waitcnt(0);   // operands in registers before any tile DMA is counted
 
     // DMA of tile j into buf: two instructions per wave, 4 key rows each
@@ -531,17 +539,18 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
         bf16x8 kf0[8], kf1[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) kf0[ks] = *(const bf16x8*)(buf + roff[ks]);
-        if (two) {
-#pragma unroll
-            for (int ks = 0; ks < 8; ks++) kf1[ks] = *(const bf16x8*)(buf + 8192 + roff[ks]);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the subtile-1 operands are read one per MFMA of the first chain: at most 8 LDS reads are
+        // outstanding, so each MFMA waits for its own operand only (lgkmcnt counts to 15)
+        auto rd1 = [&](int ks) { kf1[ks] = *(const bf16x8*)(buf + 8192 + roff[ks]); };
+        auto none_pre = [](int) {};
         float sum0 = 0.0f, sum1 = 0.0f;
         const f32x16 none = {};
-        f32x16 x = pf_chain<false>(qf[0], kf0, none, wr[0], sum0);
-        if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf0, x, wr[0], sum0);
+        f32x16 x = pf_chain<false>(qf[0], kf0, none, wr[0], sum0, rd1);
+        if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf0, x, wr[0], sum0, none_pre);
         if (two) {
-            x = pf_chain<true>(qf[0], kf1, x, wr[NHS - 1], sum0);
-            if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf1, x, wr[0], sum1);
+            x = pf_chain<true>(qf[0], kf1, x, wr[NHS - 1], sum0, none_pre);
+            if constexpr (NHS == 2) x = pf_chain<true>(qf[1], kf1, x, wr[0], sum1, none_pre);
             sum1 = pf_epilogue(x, wr[NHS - 1], sum1);
         } else {
             sum0 = pf_epilogue(x, wr[NHS - 1], sum0);
