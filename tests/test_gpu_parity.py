@@ -166,6 +166,21 @@ SMALL = [
 ]
 
 
+
+def test_long_rows_two_pass_topk_forward():
+    """Rows longer than 65536 keys (128K, 100K, 70K and 65537, next to a 65536-key row and a short
+    one): with a workspace the top-k of dsa_topk and dsa_forward runs in two passes (slices, then a
+    merge of their candidates); the selected sets must still equal the oracle's on the GPU's own
+    scores bit for bit, and the rest of the chain must match as for every workload."""
+    spec = synth.Spec("long-rows-B6-paged", ctx=[131072, 100000, 65537, 70000, 3000, 90000], nq=[1, 1, 2, 1, 1, 1],
+                      idx_dtype=synth.FP8, paged=True, seed=9)
+    dp = device_problem(spec)
+    assert dp.problem.max_len > 65536
+    b = dp.batch
+    assert dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, b, spec.topk, 1) > 0      # the two-pass path is taken
+    rows = list(range(spec.T))
+    check_problem(dp, rows_idx=[0, 2, 3], rows_topk=rows, rows_mla=[0, 2, 3, 5], label=spec.name)
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_workloads_all_rows(case):
     name, ctx, nq, hi, dt, k, h, paged = case[:8]
