@@ -228,6 +228,75 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
     }
 }
 
+// Ordered compaction of a working set held in LDS of which few entries are taken (keys[i]; entry
+// i is position pos_of(i)), through bitmasks instead of per-step scans: each wave marks 64
+// consecutive entries per ballot (above the threshold / equal to it), one block-wide scan over the
+// packed per-word counts (above | equal << 16) gives every word its first output slot and the number
+// of equal entries before it, and the thread owning a word emits its taken entries in entry order.
+// Equal entries are taken while fewer than need_eq precede them, so the result is the same as
+// compact()'s.  A thread walks its word's taken entries one by one, which pays where they are
+// sparse (rows at least 8x longer than k); nw <= 64 * kTkBlock, `bits` holds 2 * 64-bit words per 64 entries.
+template <typename PosOf, typename Emit>
+__device__ __forceinline__ void compact_sparse(const uint32_t* keys, int nw, uint32_t mask, uint32_t thr,
+                                               uint32_t need_eq, int k, uint64_t* bits,
+                                               uint32_t (&wcnt)[2][kTkWaves], PosOf&& pos_of, Emit&& emit) {
+    constexpr int kMarkUnroll = 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwords = (nw + 63) >> 6;
+    // 1. marks: bits[2c] = entries 64c .. 64c+63 above thr, bits[2c + 1] = equal to thr
+    for (int c0 = wave; c0 < nwords; c0 += kTkWaves * kMarkUnroll) {
+        uint32_t v[kMarkUnroll];
+#pragma unroll
+        for (int u = 0; u < kMarkUnroll; u++) v[u] = keys[min(64 * (c0 + u * kTkWaves) + lane, max(nw - 1, 0))] & mask;
+#pragma unroll
+        for (int u = 0; u < kMarkUnroll; u++) {
+            const int c = c0 + u * kTkWaves;
+            const bool ok = 64 * c + lane < nw;
+            const uint64_t g = __ballot(ok && v[u] > thr);
+            const uint64_t e = __ballot(ok && v[u] == thr);
+            if (lane == 0 && c < nwords) {
+                bits[2 * c] = g;
+                bits[2 * c + 1] = e;
+            }
+        }
+    }
+    __syncthreads();
+    // 2. word tid: its first slot and the equal entries before it
+    uint64_t g = 0, e = 0;
+    if (tid < nwords) {
+        g = bits[2 * tid];
+        e = bits[2 * tid + 1];
+    }
+    const uint32_t own = (uint32_t)__popcll(g) | ((uint32_t)__popcll(e) << 16);   // sums stay < 2^16 each
+    const uint32_t incl = wave_incl_scan(own);
+    if (lane == 63) wcnt[0][wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - own;
+    for (int w = 0; w < wave; w++) before += wcnt[0][w];
+    const uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
+    uint64_t take = g;
+    if (e != 0) {
+        const uint32_t quota = need_eq > eq_before ? need_eq - eq_before : 0u;
+        if (quota >= (uint32_t)__popcll(e)) {
+            take |= e;
+        } else {
+            for (uint32_t r = 0; r < quota; r++) {   // the lowest `quota` equal entries of the word
+                const uint64_t low = e & (~e + 1);
+                take |= low;
+                e ^= low;
+            }
+        }
+    }
+    // 3. emit in entry order
+    uint32_t at = gt_before + min(eq_before, need_eq);
+    while (take != 0) {
+        const int i = 64 * tid + __builtin_ctzll(take);
+        take &= take - 1;
+        if (at < (uint32_t)k) emit(at, pos_of(i), keys[i]);
+        at++;
+    }
+}
+
 // Long rows in two passes (workspace): slice s of row t (positions [s * len, (s + 1) * len)) keeps
 // its own best kt entries as (key, position) candidates -- the row's best kt are among the union of
 // the slices' best kt under the same order -- and one workgroup per row then selects from at most
@@ -251,7 +320,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
                                                         TkSlices sl) {
     // cached rows: keys[kCap]; long rows: candidate keys [0, kCandCap) + positions [kCandCap, kCap)
     extern __shared__ __align__(16) uint32_t lds[];
-    __shared__ uint32_t hist[kHistCopies][kBins];   // copies shared by alternate waves (fewer collisions)
+    __shared__ __align__(16) uint32_t hist[kHistCopies][kBins];   // copies shared by alternate waves (fewer collisions)
     __shared__ uint32_t red[2][kTkWaves];
     __shared__ uint32_t sel[3];
     __shared__ uint32_t wcnt[2][kTkWaves];
@@ -502,8 +571,18 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     // exit, where the bin holds exactly `remaining` keys).  (All keys equal: the first k.)
     const uint32_t thr = prefix, need_eq = remaining;
 
+    // a working set in LDS of which at most an eighth is taken is compacted through bitmasks (kept
+    // in the histogram's space, which the selection no longer needs)
+    static_assert(2 * (kCap / 64) * 2 <= kHistCopies * kBins, "bitmasks must fit the histogram space");
+    auto pos_of = [&](int i) -> int { return mode == kModeCand ? cpos[i] : i; };
+    auto compact_any = [&](int kk, auto&& emit) {
+        if (mode != kModeGlobal && nw >= 8 * kk)
+            compact_sparse(lds, nw, mask, thr, need_eq, kk, reinterpret_cast<uint64_t*>(&hist[0][0]), wcnt, pos_of, emit);
+        else
+            compact(key4, pos4, nw, mask, thr, need_eq, kk, wcnt, emit);
+    };
     if (PASS == 1) {   // the slice's best kts as candidates, in position order
-        compact(key4, pos4, nw, mask, thr, need_eq, kts, wcnt, [&](uint32_t at, int pos, uint32_t key) {
+        compact_any(kts, [&](uint32_t at, int pos, uint32_t key) {
             sl.ckey[cbase + at] = key;
             sl.cpos[cbase + at] = s0 + pos;
         });
@@ -513,7 +592,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
     if (tid == 0) first_win = (uint32_t)kt;   // ordered before compact's writes by its barrier
     // positions in the window [wlo, n) are written with the window block; the first of them marks
     // where that block starts
-    compact(key4, pos4, nw, mask, thr, need_eq, kt, wcnt, [&](uint32_t at, int pos, uint32_t) {
+    compact_any(kt, [&](uint32_t at, int pos, uint32_t) {
         if (pos < wlo) orow[at] = pos;
         else atomicMin(&first_win, at);
     });
