@@ -111,7 +111,7 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
  *   indices  [T][k] int32: the selected positions in ascending order, then -1 padding (n_t < k)
  * Scores are compared as real numbers (+0 == -0); equal scores go to the lower position.  NaN scores
  * are not supported.  workspace may be NULL: then each row is selected by one workgroup.  With a
- * workspace of dsa_workspace_size(DSA_OP_TOPK, ...) bytes (non-zero for rows longer than 65536),
+ * workspace of dsa_workspace_size(DSA_OP_TOPK, ...) bytes (non-zero for rows longer than 32768),
  * long rows go through two passes -- slices of the row each keep their best k (key, position)
  * candidates, then one workgroup per row selects from those -- with the same result. */
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,

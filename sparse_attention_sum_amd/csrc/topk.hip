@@ -35,7 +35,7 @@ constexpr int kDigitBits = 11; // radix digit width
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kHistCopies = 2;
 constexpr int kGatherKeys = 16;  // consecutive keys per thread per step of the candidate gather
-constexpr int kTwoPassMin = 65536;   // rows longer than this go through two passes (given a workspace)
+constexpr int kTwoPassMin = 32768;   // rows longer than this go through two passes (given a workspace)
 
 enum { kModeCached = 0, kModeGlobal = 1, kModeCand = 2 };
 

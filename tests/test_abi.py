@@ -136,7 +136,7 @@ def test_workspace_sizes(lib):
     assert lib.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512) == 0
     assert lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512) == 0
     assert lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, None, 2048, 128, 512) == 0
-    # rows longer than 65536 keys: the top-k runs in two passes and needs room for the slices'
+    # rows longer than 32768 keys: the top-k runs in two passes and needs room for the slices'
     # candidates, 4 slices of 32768 keys x k (key, position) pairs per row at 131072
     b = _batch(T=64, B=64, max_len=131072, max_q=1)
     tk = lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512)
@@ -144,8 +144,10 @@ def test_workspace_sizes(lib):
     mla = lib.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, ctypes.byref(b), 2048, 128, 512)
     fwd = lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, ctypes.byref(b), 2048, 128, 512)
     assert fwd >= max(tk, mla) + 64 * 131072 * 4 + 64 * 2048 * 4
-    b = _batch(T=64, B=64, max_len=65536, max_q=1)
+    b = _batch(T=64, B=64, max_len=32768, max_q=1)
     assert lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512) == 0
+    b = _batch(T=64, B=64, max_len=65536, max_q=1)                 # two slices of 32768
+    assert lib.dsa_workspace_size(dsa.DSA_OP_TOPK, ctypes.byref(b), 2048, 128, 512) >= 64 * 2 * 2048 * 8
 
 
 def _append(lib, k_new=FAKE, k_dtype=dsa.DSA_F32, lat=FAKE, lat_dtype=dsa.DSA_BF16, T=4, B=2, kc=None, lc=None,

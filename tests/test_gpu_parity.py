@@ -168,14 +168,14 @@ SMALL = [
 
 
 def test_long_rows_two_pass_topk_forward():
-    """Rows longer than 65536 keys (128K, 100K, 70K and 65537, next to a 65536-key row and a short
-    one): with a workspace the top-k of dsa_topk and dsa_forward runs in two passes (slices, then a
+    """Rows longer than 65536 keys (128K, 100K, 90K, 70K and 65537, next to a 65536-key row and a
+    short one): with a workspace the top-k of dsa_topk and dsa_forward runs in two passes (slices, then a
     merge of their candidates); the selected sets must still equal the oracle's on the GPU's own
     scores bit for bit, and the rest of the chain must match as for every workload."""
     spec = synth.Spec("long-rows-B6-paged", ctx=[131072, 100000, 65537, 70000, 3000, 90000], nq=[1, 1, 2, 1, 1, 1],
                       idx_dtype=synth.FP8, paged=True, seed=9)
     dp = device_problem(spec)
-    assert dp.problem.max_len > 65536
+    assert dp.problem.max_len > 32768
     b = dp.batch
     assert dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, b, spec.topk, 1) > 0      # the two-pass path is taken
     rows = list(range(spec.T))
