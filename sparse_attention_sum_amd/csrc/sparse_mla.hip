@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(const uint16_
                                                                    int H, int T, uint16_t* __restrict__ out,
                                                                    float* __restrict__ lse) {
     __shared__ float wts[kMaxSplitsComb][kHeadsPerGroup];
+    __shared__ float lsv[kMaxSplitsComb][kHeadsPerGroup];
     const int ns = S > 0 ? S : splits;
     const int hp = (H + kHeadsPerGroup - 1) / kHeadsPerGroup * kHeadsPerGroup;   // padded heads
     const int ngroups = hp / kHeadsPerGroup;
@@ -501,15 +502,19 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(const uint16_
 #pragma unroll
         for (int s = 0; s < S; s++) raw[s] = *(const i32x4*)(src + s * sstride);
     }
+    // the group's split log-sum-exps, loaded once by the whole workgroup (not split by split)
+    for (int q = tid; q < ns * kHeadsPerGroup; q += kCombThreads)
+        lsv[q / kHeadsPerGroup][q % kHeadsPerGroup] =
+            part_lse[((int64_t)t * ns + q / kHeadsPerGroup) * hp + kHeadsPerGroup * hg + q % kHeadsPerGroup];
+    __syncthreads();
     if (tid < kHeadsPerGroup) {
         const int head = kHeadsPerGroup * hg + tid;
-        const float* pl = part_lse + (int64_t)t * ns * hp + head;
         float m = -INFINITY;
-        for (int s = 0; s < ns; s++) m = fmaxf(m, pl[(int64_t)s * hp]);
+        for (int s = 0; s < ns; s++) m = fmaxf(m, lsv[s][tid]);
         float wsum = 0.0f;
-        for (int s = 0; s < ns; s++) wsum += m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m);
+        for (int s = 0; s < ns; s++) wsum += m == -INFINITY ? 0.0f : expf(lsv[s][tid] - m);
         const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-        for (int s = 0; s < ns; s++) wts[s][tid] = m == -INFINITY ? 0.0f : expf(pl[(int64_t)s * hp] - m) * inv;
+        for (int s = 0; s < ns; s++) wts[s][tid] = m == -INFINITY ? 0.0f : expf(lsv[s][tid] - m) * inv;
         if (lse && part == 0 && head < H) lse[(int64_t)t * H + head] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
     }
     __syncthreads();
@@ -528,7 +533,16 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine_kernel(const uint16_
 #pragma unroll
         for (int s = 0; s < S; s++) fold(raw[s], s);
     } else {
-        for (int s = 0; s < ns; s++) fold(*(const i32x4*)(src + s * sstride), s);
+        // batches of 8 loads in flight (clamped to the last split; the surplus is not folded)
+        constexpr int kB = 8;
+        for (int s0 = 0; s0 < ns; s0 += kB) {
+            i32x4 r[kB];
+#pragma unroll
+            for (int u = 0; u < kB; u++) r[u] = *(const i32x4*)(src + min(s0 + u, ns - 1) * sstride);
+#pragma unroll
+            for (int u = 0; u < kB; u++)
+                if (s0 + u < ns) fold(r[u], s0 + u);
+        }
     }
     const int dim = 32 * nd + (L & 31);
 #pragma unroll
