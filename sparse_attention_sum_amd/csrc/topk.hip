@@ -89,16 +89,28 @@ __device__ __forceinline__ void for_each_raw(const float* __restrict__ srow, int
                                [&](int i, const uint4& kk) { f(i, kk.x); f(i + 1, kk.y); f(i + 2, kk.z); f(i + 3, kk.w); }, f);
 }
 
-// The same over keys held in LDS (16-byte reads; the array is 16-byte aligned).
+// The same over keys held in LDS (16-byte reads; the array is 16-byte aligned).  Four reads are
+// issued before any f: one at a time, each read also queued behind the LDS atomics of the f calls
+// before it.  Reads past the end are clamped to the last aligned group (in bounds, not used).
 template <typename F>
 __device__ __forceinline__ void for_each_lds(const uint32_t* keys, int n, F&& f) {
+    constexpr int U = 4;
     const int tid = threadIdx.x;
-    for (int i = 4 * tid; i < n; i += 4 * kTkBlock) {
-        const uint4 v = *(const uint4*)(keys + i);
-        f(i, v.x);
-        if (i + 1 < n) f(i + 1, v.y);
-        if (i + 2 < n) f(i + 2, v.z);
-        if (i + 3 < n) f(i + 3, v.w);
+    const int last = max(n - 1, 0) & ~3;
+    for (int i0 = 4 * tid; i0 < n; i0 += 4 * kTkBlock * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) v[u] = *(const uint4*)(keys + min(i0 + 4 * kTkBlock * u, last));
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = i0 + 4 * kTkBlock * u;
+            if (i < n) {
+                f(i, v[u].x);
+                if (i + 1 < n) f(i + 1, v[u].y);
+                if (i + 2 < n) f(i + 2, v[u].z);
+                if (i + 3 < n) f(i + 3, v[u].w);
+            }
+        }
     }
 }
 
