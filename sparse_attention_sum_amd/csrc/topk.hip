@@ -393,26 +393,38 @@ __global__ __launch_bounds__(kTkBlock) void topk_kernel(const float* __restrict_
         }
         __syncthreads();
         nw = coff[sl.nslices];
-        // entry i of the row's candidate list is entry i - coff[s] of slice s (coff[s] <= i <
-        // coff[s + 1]); every load is independent, kUnroll of them per thread per step
-        for (int i0 = tid; i0 < nw; i0 += kTkBlock * kUnroll) {
+        // the row's workspace slots in order: slot q = s * k + j holds candidate j of slice s when
+        // j < ccnt[s], and it goes to list entry coff[s] + j.  Loads run over contiguous slots
+        // (kUnroll in flight per thread); a slot's slice comes from offsets held in registers.
+        int cb[kTkWaves + 1];
+#pragma unroll
+        for (int s2 = 0; s2 <= kTkWaves; s2++) cb[s2] = coff[min(s2, sl.nslices)];
+        const int tot = sl.nslices * k;
+        const int64_t src0 = (int64_t)t * sl.nslices * k;
+        for (int q0 = tid; q0 < tot; q0 += kTkBlock * kUnroll) {
             uint32_t kk[kUnroll];
             int32_t pp[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; u++) {
-                const int i = min(i0 + u * kTkBlock, nw - 1);
-                int sI = 0;
-                while (sI + 1 < sl.nslices && coff[sI + 1] <= i) sI++;
-                const int64_t src = ((int64_t)t * sl.nslices + sI) * k + (i - coff[sI]);
-                kk[u] = sl.ckey[src];
-                pp[u] = sl.cpos[src];
+                const int q = min(q0 + u * kTkBlock, tot - 1);
+                kk[u] = sl.ckey[src0 + q];
+                pp[u] = sl.cpos[src0 + q];
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; u++) {
-                const int i = i0 + u * kTkBlock;
-                if (i < nw) {
-                    keys[i] = kk[u];
-                    cpos[i] = pp[u];
+                const int q = q0 + u * kTkBlock;
+                int d0 = cb[0], d1 = cb[1], base = 0;
+#pragma unroll
+                for (int s2 = 1; s2 < kTkWaves; s2++)
+                    if (s2 < sl.nslices && q >= s2 * k) {
+                        d0 = cb[s2];
+                        d1 = cb[s2 + 1];
+                        base = s2 * k;
+                    }
+                const int d = d0 + (q - base);
+                if (q < tot && d < d1) {
+                    keys[d] = kk[u];
+                    cpos[d] = pp[u];
                     lo = min(lo, kk[u]);
                     hi = max(hi, kk[u]);
                 }
