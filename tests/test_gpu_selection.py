@@ -135,3 +135,27 @@ def test_two_pass_equals_one_pass(max_len, k):
     got = dsa.dsa_topk(sct, ld, b, k, workspace=ws).cpu().numpy()[:3]
     for r in range(3):
         assert sorted(v for v in ref[r] if v >= 0) == [v for v in got[r] if v >= 0]
+
+
+@pytest.mark.parametrize("k,window", [(2048, 0), (2048, 64), (1024, 0)])
+def test_sparse_compaction_rows_match_oracle(k, window):
+    """Single-pass rows of 16K-32K keys, of which at most an eighth is taken (the bitmask
+    compaction), with heavy ties, +-0 and an all-equal row: the selected lists must equal the
+    oracle's bit for bit (ties to the lower position, equal entries straddling 64-entry words)."""
+    rng = np.random.default_rng(k + window)
+    T, L = 24, 32768
+    q_len = rng.integers(8 * k, L + 1, T).astype(np.int32)
+    q_len[:3] = [L, 8 * k, L - 1]
+    ld = L
+    sc = np.round(rng.normal(0, 1, (T, ld)) * 16) / 16          # ~100 distinct values
+    sc[3, :] = 1.0                                             # all equal: the first k positions
+    sc[4, ::2] = -0.0
+    sc[4, 1::2] = 0.0
+    sc[5, : q_len[5]] = np.where(np.arange(q_len[5]) % 97 == 0, 3.0, 0.5)   # few above, many equal
+    log(f"case: sparse compaction k={k} window={window}")
+    sct = torch.from_numpy(sc.astype(np.float32)).cuda()
+    b = _batch(q_len, L)
+    got = dsa.dsa_topk_select(sct, ld, b, k, None, window).cpu().numpy()
+    ref = oracle.topk_select(sc.astype(np.float32).astype(np.float64), q_len, k, window=window, nthreads=8)
+    bad = [r for r in range(T) if not np.array_equal(got[r], ref[r])]
+    assert not bad, f"rows {bad[:5]} differ; first: gpu {got[bad[0]][:12]} ref {ref[bad[0]][:12]}"
