@@ -18,6 +18,11 @@
 // the bin of the k-th key, at most k plus that bin -- are gathered with their positions into LDS
 // in position order, and every later pass and the compaction run on them.  (Should the candidates
 // not fit, the row is simply re-read from global memory on each pass.)
+//
+// Rows longer than kTwoPassMin, given a workspace, take two passes instead: slices of the row, one
+// workgroup each, keep their own best k as candidates, and one workgroup per row selects from their
+// union (see TkSlices).  A working set of which at most an eighth is taken is compacted through
+// bitmasks (compact_sparse), denser ones with a scan per 256 entries (compact).
 #include "kernels.h"
 
 namespace dsa {
