@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
     DSA_OK = 0,
     DSA_ERR_INVALID_ARG = 1,   /* a pointer, size or layout argument is wrong */
-    DSA_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    DSA_ERR_UNSUPPORTED = 2,   /* a valid request the library does not implement */
     DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than dsa_workspace_size() */
     DSA_ERR_HIP = 4            /* the HIP runtime reported an error */
 } dsa_status;
