@@ -231,9 +231,10 @@ __global__ __launch_bounds__(kCwThreads) void rope_queries_kernel(
     const int64_t p = pos[t];
     const int hi_lo = (int)((int64_t)sl * Hi / ns), hi_hi = (int)((int64_t)(sl + 1) * Hi / ns);
     const int hm_lo = (int)((int64_t)sl * Hm / ns), hm_hi = (int)((int64_t)(sl + 1) * Hm / ns);
+    // the two angle tables on different waves (indexer: wave 0, MLA: from wave 1 on)
     if (qi_in != nullptr && tid < ri.dim / 2) rope_cs(p, tid, ri, cs_i[tid][0], cs_i[tid][1]);
     if (qm != nullptr)
-        for (int i = tid; i < rm.dim / 2; i += kCwThreads) rope_cs(p, i, rm, cs_m[i][0], cs_m[i][1]);
+        for (int i = tid - kWave; i >= 0 && i < rm.dim / 2; i += kCwThreads - kWave) rope_cs(p, i, rm, cs_m[i][0], cs_m[i][1]);
     __syncthreads();
     if (qi_in != nullptr) {
         for (int h0 = hi_lo + wave; h0 < hi_hi; h0 += kCwWaves * kIdxBatch) {
