@@ -192,7 +192,7 @@ def main():
         kq = torch.from_numpy(kq_np).to(dev)
     ind = torch.empty((T, width), dtype=torch.int32, device=dev)
     ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_FORWARD, b, k, H)), dtype=torch.uint8, device=dev)
-    scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
     mla_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, width, H)
     mla_ws = torch.empty(max(1, mla_ws_n), dtype=torch.uint8, device=dev)
 

@@ -98,9 +98,12 @@ typedef struct {
  *   weights  [T][n_heads] floats (any sign)
  *   k_cache  the 128-dim indexer key cache, dtype F32, BF16 or FP8_E4M3 (fp8 scales >= 0)
  *   scale    scalar multiplier of every score
- *   scores   [T][ld] floats, ld >= max_len: entry s of row t is written for s < n_t; entries at
- *            s >= n_t are left untouched (they are masked out of the selection)
- * head_dim must be 128; q_dtype must equal k_cache->dtype. */
+ *   scores   [T][ld] floats, ld >= max_len: every entry of row t is written -- the score for
+ *            s < n_t, -inf for n_t <= s < ld (the masked positions of the indexer-scoring step) --
+ *            except rows of queries the batch does not reach (a sequence number outside
+ *            [0, num_seqs), or a query outside its sequence's cu_q range), which are left untouched
+ * head_dim must be 128; q_dtype must equal k_cache->dtype.  (dsa_forward keeps its scores in the
+ * workspace and writes no masked entries: the top-k step reads positions s < n_t only.) */
 dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
                               int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache,
                               const dsa_batch* batch, float scale, float* scores, int64_t ld,

@@ -209,7 +209,7 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
     if (batch->num_queries > 0 && !scores) return fail(DSA_ERR_INVALID_ARG, "indexer: scores is NULL");
     if (ld < batch->max_len) return fail(DSA_ERR_INVALID_ARG, "indexer: ld %lld < max_len %d", (long long)ld, batch->max_len);
     return hip_status(dsa::launch_indexer(q, q_dtype, q_scale, weights, n_heads, view(k_cache), view(batch), scale,
-                                          scores, ld, 0, stream),
+                                          scores, ld, 0, 1, stream),
                       "indexer launch");
 }
 
@@ -289,7 +289,7 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
     const dsa::BatchView bv = view(batch);
     if (need_scores) {
         s = hip_status(dsa::launch_indexer(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, view(k_cache), bv,
-                                           idx_scale, scores, ld, k, stream),
+                                           idx_scale, scores, ld, k, 0, stream),
                        "forward: indexer launch");
         if (s != DSA_OK) return s;
     }

@@ -29,6 +29,18 @@ namespace {
 // instruction; fmaxf would add a canonicalising max in IEEE mode.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// The masked entries of a score row: -inf over positions [lo, hi), written by nthr threads (thread
+// index tid).  A call owns the rows (or the part of a row) it masks, so these stores never meet a
+// score store.
+__device__ __forceinline__ void write_masked(float* row, int64_t lo, int64_t hi, int tid, int nthr) {
+    for (int64_t s = lo + tid; s < hi; s += nthr) row[s] = -INFINITY;
+}
+
+// Rows of a batch whose queries see no position (max_len == 0): every entry of [0, ld) is masked.
+__global__ __launch_bounds__(256) void mask_rows_kernel(float* __restrict__ scores, int64_t ld) {
+    write_masked(scores + (int64_t)blockIdx.x * ld, 0, ld, threadIdx.x, 256);
+}
+
 // ---------------------------------------------------------------------------------------------
 // generic path
 
@@ -36,7 +48,8 @@ constexpr int kGenBlock = 256;
 
 __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
     const void* __restrict__ q, int dtype, const float* __restrict__ q_scale, const float* __restrict__ w,
-    int H, CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    int H, CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le,
+    int mask) {
     extern __shared__ float gsm[];
     float* qs = gsm;                 // [H][128], q * q_scale
     float* wsh = gsm + H * kIdxDim;  // [H]
@@ -44,8 +57,12 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
     const int b = bv.q_seq[t];
     if (b < 0 || b >= bv.B) return;
     const int n = min(bv.q_len[t], bv.max_len);
-    if (n <= skip_le) return;
     const int s0 = blockIdx.y * kGenBlock;
+    if (mask) {   // this block's positions past n (the last block also takes [grid end, ld))
+        const int64_t hi = blockIdx.y + 1 == gridDim.y ? ld : min(ld, (int64_t)s0 + kGenBlock);
+        write_masked(scores + (int64_t)t * ld, max((int64_t)s0, (int64_t)max(n, 0)), hi, threadIdx.x, kGenBlock);
+    }
+    if (n <= skip_le) return;
     if (s0 >= n) return;
     for (int i = threadIdx.x; i < H * kIdxDim; i += kGenBlock) {
         const int j = i / kIdxDim;
@@ -101,7 +118,7 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, f32x1
 template <int NHS, int QG>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
     constexpr int H = 32 * NHS;
     constexpr int PF = QG == 1 ? 4 : 3;   // two queries need more registers: one subtile less
     constexpr int kSub = kDecKeysPerWave / 32;
@@ -125,6 +142,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
         int nmax = n[0];
 #pragma unroll
         for (int u = 1; u < QG; u++) nmax = max(nmax, n[u]);
+        if (mask) {   // this block's positions past n (the last block also takes [grid end, ld))
+            const int64_t blo = (int64_t)blockIdx.x * (kDecWaves * kDecKeysPerWave);
+            const int64_t bhi = blockIdx.x + 1 == gridDim.x ? ld : min(ld, blo + kDecWaves * kDecKeysPerWave);
+            for (int u = 0; u < nq; u++)
+                write_masked(scores + (int64_t)(t0 + u) * ld, max(blo, (int64_t)max(n[u], 0)), bhi, threadIdx.x,
+                             kDecWaves * 64);
+        }
         if (key0 >= nmax) continue;
 
         // storage rows of the wave's subtiles: lane (g, c) reads key key0 + 32*sub + c
@@ -253,7 +277,7 @@ __device__ __forceinline__ f32x16 mfma_bf16_32(const bf16x8& a, const bf16x8& b,
 template <int NHS>
 __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le) {
+    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
     constexpr int H = 32 * NHS;
     constexpr int kChunksPerThread = kPreTile * 16 / (kPreWaves * 64);   // 16-byte chunks
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[2][kPreTile * kPreRowB];
@@ -276,7 +300,14 @@ __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
     if (lane == 0) atomicMax(&nmax_sh, n);
     __syncthreads();
     const int nmax = nmax_sh;
-    if (nmax == 0) return;
+    // the wave's own row past n (written after the scores, or now when no query of the block has any)
+    auto mask_row = [&]() {
+        if (mask && has_q) write_masked(scores + (int64_t)t * ld, max(n, 0), ld, lane, 64);
+    };
+    if (nmax == 0) {
+        mask_row();
+        return;
+    }
 
     bf16x8 qf[NHS][8];
     float wr[NHS][16];
@@ -354,6 +385,7 @@ __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
+    mask_row();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -429,7 +461,7 @@ template <int NHS>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ q_scale,
                                 const float* __restrict__ w, CacheView kc, BatchView bv, float scale,
-                                float* __restrict__ scores, int64_t ld, int skip_le) {
+                                float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
     constexpr int H = 32 * NHS;
     __shared__ __attribute__((aligned(1024))) uint8_t tile_a[kPfTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t tile_b[kPfTileBytes];
@@ -456,7 +488,15 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
     if (lane == 0) atomicMax(&nmax_sh, n);
     __syncthreads();
     const int nmax = nmax_sh;
-    if (nmax == 0) return;
+    // the wave's own row past n: written after the loop (its stores then never sit between the tile
+    // DMAs and the explicit waits for them), or now when no query of the block has a position
+    auto mask_row = [&]() {
+        if (mask && has_q) write_masked(scores + (int64_t)t * ld, n, ld, lane, 64);
+    };
+    if (nmax == 0) {
+        mask_row();
+        return;
+    }
     const int ntiles = (nmax + kPfTile - 1) / kPfTile;
     const bool paged = kc.page_table != nullptr;
     if (paged) {
@@ -583,14 +623,22 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
         if (j + 2 < ntiles) step(j + 2, tile_c, tile_b);
     }
     flush();
+    mask_row();
 }
 
 }  // namespace
 
 hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const float* w, int H,
                           const CacheView& kc, const BatchView& bv, float scale, float* scores,
-                          int64_t ld, int skip_le, hipStream_t st) {
-    if (bv.T == 0 || bv.max_len == 0 || bv.max_len <= skip_le) return hipSuccess;
+                          int64_t ld, int skip_le, int mask, hipStream_t st) {
+    if (bv.T == 0) return hipSuccess;
+    if (mask) skip_le = 0;   // every row is written whole
+    if (bv.max_len == 0) {
+        if (!mask || ld == 0) return hipSuccess;
+        mask_rows_kernel<<<bv.T, 256, 0, st>>>(scores, ld);
+        return hipGetLastError();
+    }
+    if (bv.max_len <= skip_le) return hipSuccess;
     const int nhs = (H % 32 == 0) ? H / 32 : 0;
     if (dtype == DSA_FP8_E4M3 && (nhs == 1 || nhs == 2) && bv.max_q <= 8) {
         dim3 grid((bv.max_len + kDecWaves * kDecKeysPerWave - 1) / (kDecWaves * kDecKeysPerWave), bv.B);
@@ -598,14 +646,14 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
         const int block = kDecWaves * 64;
         if (bv.max_q == 1) {
             if (nhs == 1)
-                indexer_fp8_decode_kernel<1, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                indexer_fp8_decode_kernel<1, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
             else
-                indexer_fp8_decode_kernel<2, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                indexer_fp8_decode_kernel<2, 1><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         } else {
             if (nhs == 1)
-                indexer_fp8_decode_kernel<1, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                indexer_fp8_decode_kernel<1, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
             else
-                indexer_fp8_decode_kernel<2, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                indexer_fp8_decode_kernel<2, 2><<<grid, block, 0, st>>>(q8, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         }
         return hipGetLastError();
     }
@@ -615,20 +663,20 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
         dim3 grid((bv.max_q + kPfWaves - 1) / kPfWaves, bv.B);
         if (nhs == 1)
             indexer_bf16_stream_kernel<1><<<grid, kPfWaves * 64, 0, st>>>(
-                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         else
             indexer_bf16_stream_kernel<2><<<grid, kPfWaves * 64, 0, st>>>(
-                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         return hipGetLastError();
     }
     if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2)) {
         dim3 grid((bv.max_q + kPreWaves - 1) / kPreWaves, bv.B);
         if (nhs == 1)
             indexer_bf16_prefill_kernel<1><<<grid, kPreWaves * 64, 0, st>>>(
-                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         else
             indexer_bf16_prefill_kernel<2><<<grid, kPreWaves * 64, 0, st>>>(
-                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le);
+                (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         return hipGetLastError();
     }
     const size_t shm = (size_t)H * (kIdxDim + 1) * sizeof(float);
@@ -639,7 +687,7 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
     }
     dim3 grid(bv.T, (bv.max_len + kGenBlock - 1) / kGenBlock);
     indexer_generic_kernel<<<grid, kGenBlock, shm, st>>>(q, dtype, q_scale, w, H, kc, bv, scale, scores, ld,
-                                                         skip_le);
+                                                         skip_le, mask);
     return hipGetLastError();
 }
 

@@ -14,9 +14,10 @@ struct BatchView {
 };
 
 // Lightning indexer.  skip_le > 0: queries with n_t <= skip_le need no scores and may be skipped.
+// mask != 0: entries [n_t, ld) of every row are written -inf as well (skip_le is then ignored).
 hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const float* w, int H,
                           const CacheView& kc, const BatchView& bv, float scale, float* scores,
-                          int64_t ld, int skip_le, hipStream_t st);
+                          int64_t ld, int skip_le, int mask, hipStream_t st);
 
 // Top-k per query row (ascending positions, -1 padded), rows of k + window entries: query t's best
 // clamp(kq[t], 0, k) positions (k when kq is null) united with its last `window` positions.

@@ -177,12 +177,12 @@ def dsa_workspace_size(op: int, batch: Batch, k: int, n_heads: int, d_v: int = 5
 def dsa_indexer_scores(q: torch.Tensor, q_scale: Optional[torch.Tensor], weights: torch.Tensor, k_cache: Cache,
                        batch: Batch, scale: float = 1.0, scores: Optional[torch.Tensor] = None,
                        ld: Optional[int] = None, stream=None) -> torch.Tensor:
-    """q [T, H, 128]; returns scores [T, ld] float32 (entries s >= n_t untouched)."""
+    """q [T, H, 128]; returns scores [T, ld] float32 (entries s >= n_t are -inf, written by libdsa)."""
     T, H, D = q.shape
     if ld is None:
         ld = score_ld(batch)
     if scores is None:
-        scores = torch.full((T, ld), float("-inf"), dtype=torch.float32, device=q.device)
+        scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
     kc, b = k_cache.struct(), batch.struct()
     _check(load().dsa_indexer_scores(_ptr(q), dtype_code(q), _ptr(q_scale), _ptr(weights), H, D, ctypes.byref(kc),
                                       ctypes.byref(b), float(scale), _ptr(scores), int(ld), _stream(stream)))

@@ -188,6 +188,31 @@ def build(spec: Spec) -> Problem:
                    q_mla=q_mla, latent=latent, seq_stride=seq_stride, page_table=page_table)
 
 
+def small_integer_indexer(p: Problem, seed: int = 0) -> Problem:
+    """The same workload with small-integer indexer operands: q and k in {-3, ..., 3} (stored in the
+    workload's indexer dtype: float32, bf16 or e4m3 codes, all exact), every fp8 scale 1, weights in
+    {0, 1/4, 1/2, 1}.  Every product, dot product, weighted ReLU and head sum of the indexer is then a
+    multiple of 1/4 below 2^22 in magnitude, so any summation order in binary32 gives the exact value."""
+    rng = np.random.default_rng(seed)
+    s = p.spec
+    qv = rng.integers(-3, 4, size=p.q_idx.shape).astype(np.float32)
+    kv = rng.integers(-3, 4, size=p.k_idx.shape).astype(np.float32)
+    if s.idx_dtype == F32:
+        q_raw, k_raw = qv, kv
+    elif s.idx_dtype == BF16:
+        q_raw, k_raw = _bf16_bits(qv), _bf16_bits(kv)
+    else:
+        to8 = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        q_raw, k_raw = to8(qv), to8(kv)
+    w = rng.choice(np.array([0.0, 0.25, 0.5, 1.0], np.float32), size=p.w.shape)
+    fp8 = s.idx_dtype == FP8
+    return dataclasses.replace(
+        p, q_idx=q_raw, k_idx=k_raw, w=w,
+        q_idx_scale=np.ones(p.q_idx.shape[:2], np.float32) if fp8 else None,
+        k_idx_scale=np.ones(p.k_idx.shape[0], np.float32) if fp8 else None,
+        spec=dataclasses.replace(s, idx_scale=1.0))
+
+
 # ----------------------------------------------------------------------------------------------
 # the five workloads and their variants
 
@@ -234,5 +259,5 @@ def peaked_spec() -> Spec:
     return dataclasses.replace(s, name="tiny-prefill-peaked", mla_q_sigma=72.0)
 
 
-__all__ = ["Spec", "Problem", "build", "spec_for", "sweep_spec", "peaked_spec", "ragged_lengths",
+__all__ = ["Spec", "Problem", "build", "spec_for", "sweep_spec", "peaked_spec", "ragged_lengths", "small_integer_indexer",
            "F32", "BF16", "FP8", "D_INDEX", "D_QK", "D_V", "PAGE"]

@@ -43,8 +43,10 @@ def oracle_mla(p, idx, qsel=None):
 
 
 def check_scores(gpu, ref, A, q_len_rows, rtol):
-    """|g - o| <= rtol * A on every visible entry (A: the dot products' condition magnitude)."""
-    worst = 0.0
+    """|g - o| <= rtol * A on every visible entry (A: the dot products' condition magnitude).
+    Returns (max |g - o| / A, max |g - o| / |o| over the entries with |o| >= 1e-2 A); the second is
+    the relative error reported beside the bar, on the scores that are not cancellations."""
+    worst = rel = 0.0
     for r in range(gpu.shape[0]):
         n = int(q_len_rows[r])
         g = gpu[r, :n].astype(np.float64)
@@ -55,7 +57,20 @@ def check_scores(gpu, ref, A, q_len_rows, rtol):
         assert not bad.any(), f"row {r}: {bad.sum()} scores off, worst {err[bad].max()} vs A {a[bad][0]}"
         ratio = err / np.maximum(a, 1e-30)
         worst = max(worst, float(ratio.max()) if n else 0.0)
-    return worst
+        big = np.abs(o) >= 1e-2 * a
+        if big.any():
+            rel = max(rel, float((err[big] / np.abs(o[big])).max()))
+    return worst, rel
+
+
+def recall(gpu_idx, want_idx):
+    """Mean fraction of each row's wanted positions that the GPU selected."""
+    fr = []
+    for g, w in zip(gpu_idx, want_idx):
+        ws = set(int(v) for v in w if v >= 0)
+        if ws:
+            fr.append(len(ws & set(int(v) for v in g if v >= 0)) / len(ws))
+    return float(np.mean(fr)) if fr else 1.0
 
 
 def check_mla(out_gpu, lse_gpu, out_ref, lse_ref, label=""):

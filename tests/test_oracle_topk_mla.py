@@ -253,3 +253,38 @@ def test_forward_selects_indexer_topk_when_context_exceeds_k():
         assert sorted(idx[t][idx[t] >= 0].tolist()) == sorted(want)
     o2, l2 = oracle.sparse_mla(q, lat, q_seq, q_len, idx, seq_stride=L)
     np.testing.assert_array_equal(out, o2)
+
+
+def test_peaked_head_distinct_outputs_expose_head_and_split_merge_slips():
+    """The GPU's sparse-MLA bars (max-abs 2e-2, mean-abs 5e-3, relative RMS 1e-2) on head-distinct,
+    peaked logits (each head's query drawn with sigma 72, 2048 rows selected): a kernel that gives a
+    head its neighbour's output, or merges the splits of a query with equal weights instead of the
+    log-sum-exp weights, fails them.  The log-sum-exp merge of the oracle's per-split results equals
+    the oracle on the whole list (the identity o = sum_s e^(lse_s - lse) o_s)."""
+    from helpers import check_mla, oracle_mla
+    from sparse_attention_sum_amd import synth
+
+    spec = synth.Spec("peaked-heads", ctx=[4096] * 4, nq=[1] * 4, idx_dtype=synth.FP8, topk=2048, mla_heads=128,
+                      mla_q_sigma=72.0, seed=41)
+    p = synth.build(spec)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(4096, 2048, replace=False) for _ in range(4)]).astype(np.int32)
+    o, l = oracle_mla(p, idx)
+    with pytest.raises(AssertionError):
+        check_mla(o[:, np.roll(np.arange(128), 1)], None, o, None, "neighbour head")
+    S, per = 4, 2048 // 4
+    parts, lses = [], []
+    for s in range(S):
+        part = np.full_like(idx, -1)
+        part[:, s * per:(s + 1) * per] = idx[:, s * per:(s + 1) * per]
+        o_s, l_s = oracle_mla(p, part)
+        parts.append(o_s)
+        lses.append(l_s)
+    parts, lses = np.stack(parts), np.stack(lses)
+    wts = np.exp(lses - lses.max(axis=0))
+    wts /= wts.sum(axis=0)
+    merged = (wts[..., None] * parts).sum(axis=0)
+    assert np.abs(merged - o).max() <= 1e-12 * np.abs(o).max()
+    assert np.allclose(np.log(np.exp(lses - lses.max(0)).sum(0)) + lses.max(0), l, rtol=0, atol=1e-12)
+    with pytest.raises(AssertionError):
+        check_mla(parts.mean(axis=0), None, o, None, "equal split weights")
