@@ -32,7 +32,8 @@
  *   - Argument errors are reported synchronously, before anything is launched, as DSA_ERR_INVALID_ARG
  *     or DSA_ERR_UNSUPPORTED; a failed launch is DSA_ERR_HIP.  dsa_last_error() then holds a
  *     per-thread message.  No C++ exception crosses this interface.
- *   - The library keeps no global mutable state apart from that per-thread message.
+ *   - The library keeps no global mutable state apart from that per-thread message and, for
+ *     dsa_forward_noalloc only, its static scratch array and that array's device address per GPU.
  *   - Results are deterministic: the same inputs give bitwise identical outputs.
  *   - Token positions are LOGICAL positions 0..n-1 within a sequence, independent of paging.
  *   - Device-side index data (q_len, q_seq, cu_q, page tables, selected indices) is bounds-checked
@@ -157,6 +158,22 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        const void* q, int32_t n_heads, const dsa_cache* latent, float softmax_scale,
                        const dsa_batch* batch, int32_t* indices_out, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* dsa_forward for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments as in dsa_forward, without the
+ * workspace: the call uses a scratch array of 96 MiB that the library holds in each GPU's memory
+ * from the time its code is loaded on that GPU until the process ends, and it calls no allocator.
+ * A batch whose dsa_workspace_size(DSA_OP_FORWARD, ...) exceeds 96 MiB is rejected with
+ * DSA_ERR_WORKSPACE before anything is launched (64 decode queries fit up to about 96K context each;
+ * long prefills do not fit: use dsa_forward there).  Every call on one GPU shares that GPU's array:
+ * calls that can overlap on one GPU -- on different streams, or from different threads without
+ * ordering -- race and must be serialised by the caller (one stream, or events).  The first call on
+ * a device looks up the array's device address (hipGetSymbolAddress) with that device current. */
+dsa_status dsa_forward_noalloc(const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale,
+                               const float* weights, int32_t idx_heads, const dsa_cache* k_cache, float idx_scale,
+                               int32_t k, const void* q, int32_t n_heads, const dsa_cache* latent,
+                               float softmax_scale, const dsa_batch* batch, int32_t* indices_out, void* out,
+                               float* lse, hipStream_t stream);
 
 /* Value restore after sparse MLA in MQA form (page "DeepSeek-V3.2加速技术详解", section 3.1
  * "MHA版MLA VS MQA版MLA": attention runs on the shared latent vectors and each head's value is

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cstdarg>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -157,6 +158,96 @@ dsa_status check_write_cache(const dsa_cache* c, int dim, const char* name) {
 
 bool src_dtype_ok(int32_t d) { return d == DSA_F32 || d == DSA_BF16; }
 
+// ---- the forward: argument checks and workspace size, then the launches ----
+
+// Checks the forward's arguments; *need receives the workspace bytes the batch needs.
+dsa_status forward_check(const void* q_idx, int32_t q_idx_dtype, const float* weights, int32_t idx_heads,
+                         const dsa_cache* k_cache, int32_t k, const void* q, int32_t n_heads, const dsa_cache* latent,
+                         float softmax_scale, const dsa_batch* batch, int32_t* indices_out, void* out, size_t* need) {
+    dsa_status s = check_mla(q, n_heads, dsa::kDqk, dsa::kDv, latent, batch, k, out, softmax_scale);
+    if (s != DSA_OK) return s;
+    if (batch->max_len > k) {
+        s = check_indexer(q_idx, q_idx_dtype, weights, idx_heads, dsa::kIdxDim, k_cache, batch);
+        if (s != DSA_OK) return s;
+    }
+    const int T = batch->num_queries;
+    *need = 0;
+    if (T == 0) return DSA_OK;
+    const size_t score_bytes = batch->max_len > k ? align256((size_t)T * score_ld(batch) * sizeof(float)) : 0;
+    const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
+    const size_t shared_bytes = std::max(align256(dsa::mla_workspace_bytes(T, k, n_heads)),   // top-k, then MLA
+                                         align256(dsa::topk_workspace_bytes(view(batch), k)));
+    *need = score_bytes + idx_bytes + shared_bytes;
+    return DSA_OK;
+}
+
+// Indexer (queries with n_t <= k skipped) -> top-k -> sparse MLA on `stream`, with the workspace
+// laid out as [scores][indices (unless indices_out)][top-k candidates, later the MLA split partials].
+dsa_status forward_launch(const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale, const float* weights,
+                          int32_t idx_heads, const dsa_cache* k_cache, float idx_scale, int32_t k, const void* q,
+                          int32_t n_heads, const dsa_cache* latent, float softmax_scale, const dsa_batch* batch,
+                          int32_t* indices_out, void* out, float* lse, void* workspace, hipStream_t stream) {
+    const int T = batch->num_queries;
+    const bool need_scores = batch->max_len > k;
+    const int64_t ld = score_ld(batch);
+    const size_t score_bytes = need_scores ? align256((size_t)T * ld * sizeof(float)) : 0;
+    const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
+    const size_t mla_bytes = dsa::mla_workspace_bytes(T, k, n_heads);
+    const size_t topk_bytes = dsa::topk_workspace_bytes(view(batch), k);
+    uint8_t* ws = (uint8_t*)workspace;
+    float* scores = need_scores ? (float*)ws : nullptr;
+    int32_t* idx = indices_out ? indices_out : (int32_t*)(ws + score_bytes);
+    void* mla_ws = mla_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
+    void* topk_ws = topk_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
+
+    const dsa::BatchView bv = view(batch);
+    dsa_status s = DSA_OK;
+    if (need_scores) {
+        s = hip_status(dsa::launch_indexer(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, view(k_cache), bv,
+                                           idx_scale, scores, ld, k, 0, stream),
+                       "forward: indexer launch");
+        if (s != DSA_OK) return s;
+    }
+    s = hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, idx, topk_ws, topk_bytes, stream),
+                   "forward: topk launch");
+    if (s != DSA_OK) return s;
+    return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
+                                             (uint16_t*)out, lse, mla_ws, stream),
+                      "forward: sparse_mla launch");
+}
+
+// ---- the forward's static scratch (dsa_forward_noalloc) ----
+//
+// One array per GPU, in the library's own device memory (it is allocated when the library's code
+// is loaded on a device and held until the process ends), so that dsa_forward_noalloc calls no
+// allocator.  In host code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is handed to kernels.  Nothing in the forward's workspace has to start at zero
+// (every word a kernel reads was written earlier in the same call), so the array is never cleared.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+dsa_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "forward_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "forward_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "forward_noalloc: hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(DSA_ERR_HIP, "forward_noalloc: no device address for the scratch array");
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,44 +352,34 @@ dsa_status dsa_forward(const void* q_idx, int32_t q_idx_dtype, const float* q_id
                        int32_t n_heads, const dsa_cache* latent, float softmax_scale, const dsa_batch* batch,
                        int32_t* indices_out, void* out, float* lse, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    dsa_status s = check_mla(q, n_heads, dsa::kDqk, dsa::kDv, latent, batch, k, out, softmax_scale);
-    if (s != DSA_OK) return s;
-    const bool need_scores = batch->max_len > k;
-    if (need_scores) {
-        s = check_indexer(q_idx, q_idx_dtype, weights, idx_heads, dsa::kIdxDim, k_cache, batch);
-        if (s != DSA_OK) return s;
-    }
-    const int T = batch->num_queries;
-    if (T == 0) return DSA_OK;
-    const int64_t ld = score_ld(batch);
     size_t need = 0;
-    const size_t score_bytes = need_scores ? align256((size_t)T * ld * sizeof(float)) : 0;
-    const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
-    const size_t mla_bytes = dsa::mla_workspace_bytes(T, k, n_heads);
-    const size_t topk_bytes = dsa::topk_workspace_bytes(view(batch), k);
-    const size_t shared_bytes = std::max(align256(mla_bytes), align256(topk_bytes));   // top-k, then MLA
-    need = score_bytes + idx_bytes + shared_bytes;
+    dsa_status s = forward_check(q_idx, q_idx_dtype, weights, idx_heads, k_cache, k, q, n_heads, latent,
+                                 softmax_scale, batch, indices_out, out, &need);
+    if (s != DSA_OK || batch->num_queries == 0) return s;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-    uint8_t* ws = (uint8_t*)workspace;
-    float* scores = need_scores ? (float*)ws : nullptr;
-    int32_t* idx = indices_out ? indices_out : (int32_t*)(ws + score_bytes);
-    void* mla_ws = mla_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
-    void* topk_ws = topk_bytes ? (void*)(ws + score_bytes + idx_bytes) : nullptr;
+    return forward_launch(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, k_cache, idx_scale, k, q, n_heads,
+                          latent, softmax_scale, batch, indices_out, out, lse, workspace, stream);
+}
 
-    const dsa::BatchView bv = view(batch);
-    if (need_scores) {
-        s = hip_status(dsa::launch_indexer(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, view(k_cache), bv,
-                                           idx_scale, scores, ld, k, 0, stream),
-                       "forward: indexer launch");
-        if (s != DSA_OK) return s;
-    }
-    s = hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, idx, topk_ws, topk_bytes, stream),
-                   "forward: topk launch");
+dsa_status dsa_forward_noalloc(const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale,
+                               const float* weights, int32_t idx_heads, const dsa_cache* k_cache, float idx_scale,
+                               int32_t k, const void* q, int32_t n_heads, const dsa_cache* latent,
+                               float softmax_scale, const dsa_batch* batch, int32_t* indices_out, void* out,
+                               float* lse, hipStream_t stream) {
+    size_t need = 0;
+    dsa_status s = forward_check(q_idx, q_idx_dtype, weights, idx_heads, k_cache, k, q, n_heads, latent,
+                                 softmax_scale, batch, indices_out, out, &need);
+    if (s != DSA_OK || batch->num_queries == 0) return s;
+    if (need > kScratchBytes)
+        return fail(DSA_ERR_WORKSPACE,
+                    "forward_noalloc: this batch needs %zu bytes of scratch, the library's static scratch holds %zu "
+                    "(use dsa_forward with a workspace)", need, kScratchBytes);
+    void* ws = nullptr;
+    s = scratch_on_current_device(&ws);
     if (s != DSA_OK) return s;
-    return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
-                                             (uint16_t*)out, lse, mla_ws, stream),
-                      "forward: sparse_mla launch");
+    return forward_launch(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, k_cache, idx_scale, k, q, n_heads,
+                          latent, softmax_scale, batch, indices_out, out, lse, ws, stream);
 }
 
 dsa_status dsa_cache_append(const void* k_new, int32_t k_new_dtype, const void* latent_new,

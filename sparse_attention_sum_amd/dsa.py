@@ -24,7 +24,7 @@ DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_workspace_size",
            "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries",
-           "dsa_topk_select", "dsa_value_restore")
+           "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc")
 
 
 class DsaError(RuntimeError):
@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
     L.dsa_value_restore.argtypes = [P, P, I32, I32, I32, P, P]
     L.dsa_sparse_mla.argtypes = [P, I32, I32, I32, CP, BP, P, I32, F, P, P, P, ctypes.c_size_t, P]
     L.dsa_forward.argtypes = [P, I32, P, P, I32, CP, F, I32, P, I32, CP, F, BP, P, P, P, P, ctypes.c_size_t, P]
+    L.dsa_forward_noalloc.argtypes = [P, I32, P, P, I32, CP, F, I32, P, I32, CP, F, BP, P, P, P, P]
     L.dsa_workspace_size.argtypes = [I32, BP, I32, I32, I32]
     RP = ctypes.POINTER(_Rope)
     L.dsa_cache_append.argtypes = [P, I32, P, I32, P, P, I32, I32, RP, RP, CP, CP, P]
@@ -97,7 +98,7 @@ def load() -> ctypes.CDLL:
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_cache_append",
-                 "dsa_rope_queries", "dsa_topk_select", "dsa_value_restore"):
+                 "dsa_rope_queries", "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -261,6 +262,22 @@ def dsa_forward(q_idx: torch.Tensor, q_idx_scale: Optional[torch.Tensor], weight
                                ctypes.byref(kc), float(idx_scale), int(k), _ptr(q), H, ctypes.byref(lc),
                                float(softmax_scale), ctypes.byref(b), _ptr(indices_out), _ptr(out), _ptr(lse),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse, indices_out
+
+
+def dsa_forward_noalloc(q_idx: torch.Tensor, q_idx_scale: Optional[torch.Tensor], weights: torch.Tensor,
+                        k_cache: Cache, k: int, q: torch.Tensor, latent: Cache, batch: Batch, softmax_scale: float,
+                        out: torch.Tensor, idx_scale: float = 1.0, indices_out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None):
+    """dsa_forward without a workspace (libdsa's static scratch); out [T, H, 512] bf16 must be given,
+    since this call allocates nothing.  Returns (out, lse, indices_out)."""
+    T, H, _ = q.shape
+    HI = int(q_idx.shape[1])
+    kc, lc, b = k_cache.struct(), latent.struct(), batch.struct()
+    _check(load().dsa_forward_noalloc(_ptr(q_idx), dtype_code(q_idx), _ptr(q_idx_scale), _ptr(weights), HI,
+                                      ctypes.byref(kc), float(idx_scale), int(k), _ptr(q), H, ctypes.byref(lc),
+                                      float(softmax_scale), ctypes.byref(b), _ptr(indices_out), _ptr(out), _ptr(lse),
+                                      _stream(stream)))
     return out, lse, indices_out
 
 

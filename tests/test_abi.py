@@ -219,3 +219,21 @@ def test_topk_select_validation(lib):
     assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 65000, None, 1000, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk_select(FAKE, 99, ctypes.byref(b), 16, None, 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk_select(FAKE, 128, ctypes.byref(b), 16, None, 0, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_forward_noalloc_rejects_a_batch_past_its_scratch(lib):
+    """dsa_forward_noalloc checks the batch's workspace against its 96 MiB static scratch on the host,
+    before any device call: 320 queries at 70000 positions need more (their scores alone are 85 MiB)."""
+    T, L = 320, 70000
+    b = dsa._Batch(T, 8, FAKE, FAKE, FAKE, L, 40)
+    kc = _cache(dim=128, rows=8 * L, stride=L)
+    lc = dsa._Cache(FAKE, None, dsa.DSA_BF16, 576, 8 * L, L, None, 0, 64)
+    assert lib.dsa_workspace_size(dsa.DSA_OP_FORWARD, ctypes.byref(b), 2048, 128, 512) > 96 << 20
+    st = lib.dsa_forward_noalloc(FAKE, dsa.DSA_FP8_E4M3, None, FAKE, 64, ctypes.byref(kc), 1.0, 2048, FAKE, 128,
+                                 ctypes.byref(lc), 1 / 24, ctypes.byref(b), None, FAKE, None, None)
+    assert st == dsa.DSA_ERR_WORKSPACE
+    assert b"scratch" in lib.dsa_last_error()
+    # argument errors come first, as in dsa_forward
+    assert lib.dsa_forward_noalloc(FAKE, dsa.DSA_FP8_E4M3, None, FAKE, 64, ctypes.byref(kc), 1.0, 0, FAKE, 128,
+                                   ctypes.byref(lc), 1 / 24, ctypes.byref(b), None, FAKE, None,
+                                   None) == dsa.DSA_ERR_INVALID_ARG
