@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--value-restore", action="store_true",
                     help="measure the value up-projection after sparse MLA (d_h = 128) on the workload's query "
                          "tokens instead of the forward; prints its own JSON line")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the decode-B64-ctx131072 block that the default workload's line carries")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--write-path", action="store_true",
                     help="measure the cache write path (query rotation + key / latent append) of the workload's "
                          "query tokens instead of the forward; prints its own JSON line")
@@ -150,6 +153,138 @@ def recorded_traffic(stage, workload):
     if not rec or rec.get("source_sha256_16") != source_hash(stage):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def achievable_peaks(dev, stream):
+    """What this GPU delivers, measured with the probe kernels (probe/libpeaks.so): a streaming read
+    of 4 GiB (GB/s) and a bf16 MFMA loop (TFLOP/s), best of 5 launches each, HIP events on `stream`."""
+    import ctypes
+    import torch
+    from sparse_attention_sum_amd import build as libbuild
+    L = ctypes.CDLL(libbuild.PROBE_LIB)
+    L.peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.peak_read.restype = L.peak_mfma_bf16.restype = ctypes.c_int
+    st = ctypes.c_void_p(stream.cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    read_blocks, mfma_blocks, iters = 256 * 16, 256 * 2, 20000
+    sink = torch.empty(read_blocks * 256, dtype=torch.int32, device=dev)
+
+    def best(fn):
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = fn()
+            e1.record(stream)
+            assert rc == 0, f"probe launch failed ({rc})"
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts[1:])
+
+    t_read = best(lambda: L.peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                      read_blocks, st))
+    t_mfma = best(lambda: L.peak_mfma_bf16(iters, ctypes.c_void_p(sink.data_ptr()), mfma_blocks, st))
+    del buf
+    flops = mfma_blocks * 4 * iters * 4 * 32768
+    return {"hbm_read_GBs": round(nbytes / t_read / 1e9, 1), "bf16_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "method": "streaming read of 4 GiB (16-byte loads, 8 in flight per thread) and a loop of "
+                      "independent 32x32x16 bf16 MFMA chains at 2 waves per SIMD; best of 5"}
+
+
+def long_context_block(dev, stream, flush, timed, steps=10):
+    """The batched-decode shape at 131072 positions (64 sequences, one query each), drawn on the
+    device: forward and per-stage times, the sparse-MLA stage's HBM fraction, and a spot check of two
+    queries against the oracle (indexer scores, the top-k set on the GPU's scores, sparse MLA on the
+    GPU's indices)."""
+    import torch
+    import oracle
+    from sparse_attention_sum_amd import dsa, synth
+
+    ctx, T, H, k = 131072, 64, 128, 2048
+    t0 = time.time()
+    d = synth.build_decode_on_device(ctx, T, seed=1, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    b = dsa.Batch(cu_q=d["cu_q"], q_seq=d["q_seq"], q_len=d["q_len"], max_len=ctx, max_q=1)
+    kc = dsa.Cache(d["k_idx"], d["k_idx_scale"], seq_stride=ctx)
+    lc = dsa.Cache(d["latent"], seq_stride=ctx)
+    scale = 1.0 / 24.0
+    ld = dsa.score_ld(b)
+    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    ind = torch.empty((T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_FORWARD, b, k, H)), dtype=torch.uint8, device=dev)
+    tk_ws_n = dsa.dsa_workspace_size(dsa.DSA_OP_TOPK, b, k, H)
+    tk_ws = torch.empty(max(1, tk_ws_n), dtype=torch.uint8, device=dev)
+    mla_ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, b, k, H)), dtype=torch.uint8,
+                         device=dev)
+    fwd = lambda: dsa.dsa_forward(d["q_idx"], d["q_idx_scale"], d["w"], kc, k, d["q_mla"], lc, b, scale,
+                                  indices_out=ind, out=out, lse=lse, workspace=ws, stream=stream)
+    stage = {
+        "indexer": lambda: dsa.dsa_indexer_scores(d["q_idx"], d["q_idx_scale"], d["w"], kc, b, 1.0, scores=scores,
+                                                  ld=ld, stream=stream),
+        "topk": lambda: dsa.dsa_topk(scores, ld, b, k, indices=ind, stream=stream, workspace=tk_ws),
+        "sparse_mla": lambda: dsa.dsa_sparse_mla(d["q_mla"], lc, b, ind, scale, out=out, lse=lse, workspace=mla_ws,
+                                                 stream=stream),
+    }
+    for _ in range(3):
+        fwd()
+    ms, _ = timed(fwd, steps)
+    res = {"workload": "decode-B64-ctx131072 (inputs drawn on the device)", "steps": steps,
+           "ms_per_step": round(float(ms.mean()), 5), "tokens_per_s": round(T / (float(ms.mean()) / 1e3), 1),
+           "stages_us": {}, "setup_s": round(gen_s, 1)}
+    for name in ("indexer", "topk", "sparse_mla"):
+        stage[name]()
+        sms, _ = timed(stage[name], steps)
+        res["stages_us"][name] = round(float(sms.mean() * 1e3), 3)
+    mla_bytes = T * k * (576 * 2 + 4) + T * H * (576 * 2 + 512 * 2 + 4)
+    idx_bytes = T * ctx * (128 + 4) + T * 64 * (128 + 8) + T * ctx * 4
+    res["sparse_mla_hbm_frac"] = round(mla_bytes / (res["stages_us"]["sparse_mla"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    res["indexer_hbm_frac"] = round(idx_bytes / (res["stages_us"]["indexer"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    # spot check of queries 0 and 63 against the oracle (their sequences copied to the host)
+    torch.cuda.synchronize()
+    check = {}
+    for t in (0, 63):
+        kq = d["q_idx"][t:t + 1].view(torch.uint8).cpu().numpy()
+        qs = d["q_idx_scale"][t:t + 1].cpu().numpy()
+        wt = d["w"][t:t + 1].cpu().numpy()
+        krows = d["k_idx"][t * ctx:(t + 1) * ctx].view(torch.uint8).cpu().numpy()
+        ksc = d["k_idx_scale"][t * ctx:(t + 1) * ctx].cpu().numpy()
+        one = dict(q_seq=np.zeros(1, np.int32), q_len=np.array([ctx], np.int32), seq_stride=ctx, nthreads=16)
+        ref = oracle.indexer(kq, "fp8", qs, wt, krows, "fp8", ksc, **one)
+        A = oracle.indexer(kq & np.uint8(0x7F), "fp8", qs, np.abs(wt), krows & np.uint8(0x7F), "fp8", ksc, **one)
+        g = scores[t, :ctx].double().cpu().numpy()
+        idx_err = float((np.abs(g - ref[0, :ctx]) / np.maximum(A[0, :ctx], 1e-30)).max())
+        assert idx_err <= 2e-2, f"long-context spot check: indexer |err|/A {idx_err}"
+        gi = ind[t].cpu().numpy()
+        want = oracle.topk(g[None], np.array([ctx], np.int32), k)[0]
+        assert sorted(gi[gi >= 0].tolist()) == sorted(want[want >= 0].tolist()), "long-context spot check: top-k"
+        sel = torch.from_numpy(gi.astype(np.int64)).to(dev) + t * ctx
+        lat = d["latent"][sel].view(torch.int16).cpu().numpy().view(np.uint16)
+        qm = d["q_mla"][t:t + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+        o_ref, _ = oracle.sparse_mla(qm, lat, np.zeros(1, np.int32), np.array([k], np.int32),
+                                     np.arange(k, dtype=np.int32)[None], seq_stride=k, softmax_scale=scale,
+                                     nthreads=16)
+        mla_err = float(np.abs(out[t].float().cpu().numpy() - o_ref[0]).max())
+        assert mla_err <= 2e-2, f"long-context spot check: sparse MLA max-abs {mla_err}"
+        check[f"query{t}"] = {"indexer_err_over_A": idx_err, "topk": "bit-exact", "mla_max_abs": mla_err}
+    res["spot_check"] = check
+    del d, ws, scores
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------------------------------
@@ -316,6 +451,12 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic}
     roofline["kernel"] = dom
+    peaks = None
+    if not args.no_peaks:
+        peaks = achievable_peaks(dev, stream)
+        ach = peaks["hbm_read_GBs"] if bound == "hbm" else peaks["bf16_mfma_TFLOPs"]
+        roofline["achievable_peak"] = ach
+        roofline["frac_of_achievable"] = round(achieved / ach, 4)
     for st, v in stages.items():
         v["hbm_GBs"] = round(v["alg_bytes"] / (v["mean_us"] * 1e-6) / 1e9, 1)
         if v["alg_flops"]:
@@ -352,7 +493,11 @@ def main():
                 break
         cpu = {"value": round(reps * len(rows) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"{len(rows)} of {T} query tokens of {args.workload} (evenly spaced), fp64 oracle forward, "
-                         f"{reps} repetition(s) in {dt:.2f} s wall"}
+                         f"{reps} repetition(s) in {dt:.2f} s wall", "cpu_model": cpu_model()}
+
+    long_ctx = None
+    if args.workload == DEFAULT_WORKLOAD and not args.no_long_context and not variant:
+        long_ctx = long_context_block(dev, stream, flush, timed)
 
     line = {
         "metric": "DSA tokens/s (indexer+top-k+sparse MLA)",
@@ -376,6 +521,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_us": stages,
+        "achievable_peaks": peaks,
+        "decode_ctx131072": long_ctx,
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "p10_p90_ms": [round(float(np.percentile(ms, 10)), 5), round(float(np.percentile(ms, 90)), 5)],
         "spot_check": check,

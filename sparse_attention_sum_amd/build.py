@@ -84,5 +84,20 @@ def build(extra_flags=(), verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libpeaks.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's achievable-peak probes (stream read, bf16 MFMA loop): probe/libpeaks.so."""
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp], "hipcc peaks.hip")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(sys.argv[1:], verbose=True)
+    build_probe(verbose=True)

@@ -251,6 +251,47 @@ def sweep_spec(ctx: int, batch: int = 64) -> Spec:
     return Spec(f"decode-B{batch}-ctx{ctx}", ctx=[ctx] * batch, nq=[1] * batch, idx_dtype=FP8, seed=1)
 
 
+def build_decode_on_device(ctx: int, batch: int = 64, seed: int = 1, device="cuda"):
+    """The batched-decode workload drawn directly in device memory (torch's seeded generator on the
+    GPU), for contexts whose host-side draw would take minutes: returns a dict of device tensors with
+    the same distributions and storage formats as build() (fp8 indexer keys and queries with one scale
+    per 128-wide row, w ~ U(0, 1), MLA q and latent ~ N(0, 1/24^2) in bf16, contiguous caches).
+    The host copies the rows it checks; the values differ from build()'s for the same seed."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    T, rows = batch, batch * ctx
+
+    def fp8_rows(shape):
+        x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        amax = x.abs().amax(dim=-1, keepdim=True)
+        scale = torch.clamp(amax, min=1e-12) / 448.0
+        codes = torch.clamp(x / scale, -448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes, scale.squeeze(-1)
+
+    def bf16_normal(shape, sigma, chunk=1 << 26):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        flat = out.view(-1)
+        for s0 in range(0, flat.numel(), chunk):
+            e = min(flat.numel(), s0 + chunk)
+            flat[s0:e] = (torch.randn(e - s0, generator=g, device=dev) * sigma).to(torch.bfloat16)
+        return out
+
+    q_idx, q_idx_scale = fp8_rows((T, 64, D_INDEX))
+    k_parts, s_parts = [], []
+    for r0 in range(0, rows, 1 << 22):
+        c, sc = fp8_rows((min(rows, r0 + (1 << 22)) - r0, D_INDEX))
+        k_parts.append(c)
+        s_parts.append(sc)
+    k_idx, k_idx_scale = torch.cat(k_parts), torch.cat(s_parts)
+    w = torch.rand((T, 64), generator=g, device=dev, dtype=torch.float32)
+    q_mla = bf16_normal((T, 128, D_QK), 1.0 / 24.0)
+    latent = bf16_normal((rows, D_QK), 1.0 / 24.0)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    return dict(ctx=ctx, T=T, B=batch, q_idx=q_idx, q_idx_scale=q_idx_scale, w=w, k_idx=k_idx,
+                k_idx_scale=k_idx_scale, q_mla=q_mla, latent=latent, seq_stride=ctx,
+                cu_q=i32(list(range(T + 1))), q_seq=i32(list(range(T))), q_len=i32([ctx] * T))
+
+
 def peaked_spec() -> Spec:
     """Tiny-prefill shapes with MLA q ~ N(0, 72^2): with latent ~ N(0, 1/24^2) and the 1/sqrt(576)
     softmax scale, each logit then has standard deviation 72 * 24 / 24 / 24 = 3, so the softmax is
