@@ -121,6 +121,23 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The indexer and the top-k step in one call: the selection of dsa_indexer_scores followed by
+ * dsa_topk, bit for bit, without handing the scores to the caller (page "DeepSeek 稀疏注意力路线（V3 /
+ * V3.2 / V4）", section "两阶段流程", items 1-2: every past token is scored and only the top-k of those
+ * scores are kept).  Arguments as in dsa_indexer_scores, plus
+ *   k        1 <= k <= 65536
+ *   indices  [T][k] int32: the selected positions in ascending order, then -1 padding
+ *   workspace  device memory of dsa_workspace_size(DSA_OP_INDEXER_TOPK, ...) bytes
+ * When the rows are longer than 32768 positions, the queries are fp8 with 32 or 64 heads, a sequence
+ * has at most two queries and pages (if any) hold at least 16 tokens, the scores never leave the chip:
+ * each workgroup scores one slice of a sequence's positions into LDS and keeps only the slice's best k
+ * as candidates, and a second pass selects each row's k from its slices' candidates.  Otherwise the
+ * scores go through the workspace (queries with n_t <= k are not scored: they select every position). */
+dsa_status dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
+                            int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache, const dsa_batch* batch,
+                            float scale, int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Selection variants of the top-k step (page "DeepSeek-V3.2推理加速引擎深度剖析", closing outlook:
  * a K chosen per query, and the sliding-window branch combined with the selection; page
  * "DeepSeek-V3.2加速技术详解": the third, sliding-window branch).
@@ -239,7 +256,7 @@ dsa_status dsa_rope_queries(const void* q_idx_in, int32_t q_idx_in_dtype, int32_
                             int32_t num_tokens, hipStream_t stream);
 
 /* Operations for dsa_workspace_size. */
-enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
+enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3, DSA_OP_INDEXER_TOPK = 4 };
 
 /* Bytes of workspace the operation needs for this batch (0 if none).  For DSA_OP_FORWARD, `k` is the
  * top-k size and indices_out is assumed NULL (the worst case). */

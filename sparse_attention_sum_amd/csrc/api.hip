@@ -160,6 +160,40 @@ bool src_dtype_ok(int32_t d) { return d == DSA_F32 || d == DSA_BF16; }
 
 // ---- the forward: argument checks and workspace size, then the launches ----
 
+// The workspace region that the top-k's candidates (unfused or fused first pass) and, after them, the
+// MLA split partials share.
+size_t forward_shared_bytes(const dsa_batch* batch, int32_t k, int32_t n_heads) {
+    const int T = batch->num_queries;
+    return std::max(std::max(align256(dsa::mla_workspace_bytes(T, k, n_heads)),
+                             align256(dsa::topk_workspace_bytes(view(batch), k))),
+                    align256(dsa::indexer_topk_workspace_bound(view(batch), k)));
+}
+
+// dsa_indexer_topk's workspace: the fused pass's candidates, or the scores then the top-k's candidates
+// (whichever is larger: the dtype and cache layout that decide between them are not known here).
+size_t indexer_topk_bytes(const dsa_batch* batch, int32_t k) {
+    const int T = batch->num_queries;
+    if (T <= 0 || batch->max_len <= k) return 0;
+    const size_t unfused = align256((size_t)T * score_ld(batch) * sizeof(float)) +
+                           align256(dsa::topk_workspace_bytes(view(batch), k));
+    return std::max(unfused, align256(dsa::indexer_topk_workspace_bound(view(batch), k)));
+}
+
+// The forward takes the fused indexer -> top-k pass where it measured faster than the unfused one:
+// one query per sequence and slices that give a workgroup to every CU.  (Measured, indexer + top-k:
+// 64 x 131072 229 us fused against 275 us; 64 x 65536 129 against 148; but 16 x 131072 117 against
+// 100, and two queries per sequence at 32 x 65536 119 against 112: fewer workgroups, or two rows per
+// slice, leave CUs idle that the unfused indexer keeps busy.)
+bool forward_fuses(int32_t q_idx_dtype, int32_t idx_heads, const dsa_cache* k_cache, const dsa_batch* batch,
+                   int32_t k) {
+    int ns = 0, slen = 0;
+    size_t bytes = 0;
+    if (batch->max_q != 1) return false;
+    if (!dsa::indexer_topk_plan(q_idx_dtype, idx_heads, view(k_cache), view(batch), k, &ns, &slen, &bytes))
+        return false;
+    return (int64_t)batch->num_seqs * ns >= 256;
+}
+
 // Checks the forward's arguments; *need receives the workspace bytes the batch needs.
 dsa_status forward_check(const void* q_idx, int32_t q_idx_dtype, const float* weights, int32_t idx_heads,
                          const dsa_cache* k_cache, int32_t k, const void* q, int32_t n_heads, const dsa_cache* latent,
@@ -175,9 +209,7 @@ dsa_status forward_check(const void* q_idx, int32_t q_idx_dtype, const float* we
     if (T == 0) return DSA_OK;
     const size_t score_bytes = batch->max_len > k ? align256((size_t)T * score_ld(batch) * sizeof(float)) : 0;
     const size_t idx_bytes = indices_out ? 0 : align256((size_t)T * k * sizeof(int32_t));
-    const size_t shared_bytes = std::max(align256(dsa::mla_workspace_bytes(T, k, n_heads)),   // top-k, then MLA
-                                         align256(dsa::topk_workspace_bytes(view(batch), k)));
-    *need = score_bytes + idx_bytes + shared_bytes;
+    *need = score_bytes + idx_bytes + forward_shared_bytes(batch, k, n_heads);
     return DSA_OK;
 }
 
@@ -202,6 +234,15 @@ dsa_status forward_launch(const void* q_idx, int32_t q_idx_dtype, const float* q
 
     const dsa::BatchView bv = view(batch);
     dsa_status s = DSA_OK;
+    if (need_scores && forward_fuses(q_idx_dtype, idx_heads, k_cache, batch, k)) {
+        s = hip_status(dsa::launch_indexer_topk((const uint8_t*)q_idx, q_idx_scale, weights, idx_heads, view(k_cache),
+                                                bv, idx_scale, k, idx, ws + score_bytes + idx_bytes, stream),
+                       "forward: fused indexer -> top-k launch");
+        if (s != DSA_OK) return s;
+        return hip_status(dsa::launch_sparse_mla((const uint16_t*)q, n_heads, view(latent), bv, idx, k, softmax_scale,
+                                                 (uint16_t*)out, lse, mla_ws, stream),
+                          "forward: sparse_mla launch");
+    }
     if (need_scores) {
         s = hip_status(dsa::launch_indexer(q_idx, q_idx_dtype, q_idx_scale, weights, idx_heads, view(k_cache), bv,
                                            idx_scale, scores, ld, k, 0, stream),
@@ -284,10 +325,10 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* batch, int32_t k, int32_t
             if (batch->max_len > k) bytes += align256((size_t)T * score_ld(batch) * sizeof(float));
             bytes += align256((size_t)T * k * sizeof(int32_t));
             // the top-k candidates and the MLA partials share one region (used one after the other)
-            bytes += std::max(align256(dsa::mla_workspace_bytes(T, k, n_heads)),
-                              align256(dsa::topk_workspace_bytes(view(batch), k)));
-            return bytes;
+            return bytes + forward_shared_bytes(batch, k, n_heads);
         }
+        case DSA_OP_INDEXER_TOPK:
+            return k > 0 ? indexer_topk_bytes(batch, k) : 0;
     }
     return 0;
 }
@@ -302,6 +343,47 @@ dsa_status dsa_indexer_scores(const void* q, int32_t q_dtype, const float* q_sca
     return hip_status(dsa::launch_indexer(q, q_dtype, q_scale, weights, n_heads, view(k_cache), view(batch), scale,
                                           scores, ld, 0, 1, stream),
                       "indexer launch");
+}
+
+dsa_status dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
+                            int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache, const dsa_batch* batch,
+                            float scale, int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    dsa_status s = check_indexer(q, q_dtype, weights, n_heads, head_dim, k_cache, batch);
+    if (s != DSA_OK) return s;
+    if (k < 1 || k > kMaxK) return fail(DSA_ERR_INVALID_ARG, "k %d not in [1, %d]", k, kMaxK);
+    if (batch->num_queries > 0 && !indices) return fail(DSA_ERR_INVALID_ARG, "indexer_topk: indices is NULL");
+    if (batch->num_queries == 0) return DSA_OK;
+    const dsa::BatchView bv = view(batch);
+    const dsa::CacheView kc = view(k_cache);
+    int ns = 0, slen = 0;
+    size_t fbytes = 0;
+    if (dsa::indexer_topk_plan(q_dtype, n_heads, kc, bv, k, &ns, &slen, &fbytes)) {
+        if (!workspace || workspace_bytes < fbytes)
+            return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace of %zu bytes needed, %zu given", fbytes,
+                        workspace_bytes);
+        return hip_status(dsa::launch_indexer_topk((const uint8_t*)q, q_scale, weights, n_heads, kc, bv, scale, k,
+                                                   indices, workspace, stream),
+                          "indexer_topk launch");
+    }
+    // unfused: the scores of the rows longer than k in the workspace, then the top-k
+    const bool need_scores = batch->max_len > k;
+    const int64_t ld = score_ld(batch);
+    const size_t score_bytes = need_scores ? align256((size_t)batch->num_queries * ld * sizeof(float)) : 0;
+    const size_t topk_bytes = dsa::topk_workspace_bytes(bv, k);
+    if (score_bytes + topk_bytes > 0 && (!workspace || workspace_bytes < score_bytes + topk_bytes))
+        return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace of %zu bytes needed, %zu given",
+                    score_bytes + topk_bytes, workspace_bytes);
+    float* scores = need_scores ? (float*)workspace : nullptr;
+    if (need_scores) {
+        s = hip_status(dsa::launch_indexer(q, q_dtype, q_scale, weights, n_heads, kc, bv, scale, scores, ld, k, 0,
+                                           stream),
+                       "indexer_topk: indexer launch");
+        if (s != DSA_OK) return s;
+    }
+    return hip_status(dsa::launch_topk(scores, ld, bv, k, nullptr, 0, indices,
+                                       topk_bytes ? (uint8_t*)workspace + score_bytes : nullptr, topk_bytes, stream),
+                      "indexer_topk: topk launch");
 }
 
 dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int32_t k, int32_t* indices,

@@ -19,15 +19,11 @@
 // The ReLU-weight-sum epilogue runs on the MFMA accumulators in registers: the 32x32 accumulator
 // layout gives every lane 16 head rows of one key column, so the head sum is 16 in-register FMAs
 // per tile plus one cross-half shuffle.
-#include "kernels.h"
+#include "indexer_fp8.h"
 
 namespace dsa {
 namespace {
 
-// max(0, x) as a signed-integer max of the bits: non-negative floats order like their bit patterns,
-// and every negative float (sign bit set) is a negative integer, which becomes +0.  One VALU
-// instruction; fmaxf would add a canonicalising max in IEEE mode.
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // The masked entries of a score row: -inf over positions [lo, hi), written by nthr threads (thread
 // index tid).  A call owns the rows (or the part of a row) it masks, so these stores never meet a
@@ -103,10 +99,6 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
 constexpr int kDecKeysPerWave = 256;
 constexpr int kDecWaves = 4;
 
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, f32x16 c) {
-    // format 0 = e4m3 for both operands; block scales 127 = 2^0.
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
 
 // QG query tokens of one sequence share each key fetch (1 for plain decode, 2 for two-token
 // speculative decode).  A wave keeps PF key subtiles (32 keys each) in flight (4, or 3 for QG = 2): the loads of subtile
@@ -238,22 +230,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
             const float ksj = ok ? ks[j] : 0.0f;
 #pragma unroll
             for (int u = 0; u < QG; u++) {
-                float sum = 0.0f;
-#pragma unroll
-                for (int hs = 0; hs < NHS; hs++) {
-                    f32x16 acc = {};
-                    acc = mfma_fp8(qf[u][hs][0], k0, acc);
-                    acc = mfma_fp8(qf[u][hs][1], k1, acc);
-#pragma unroll
-                    for (int blk = 0; blk < 4; blk++) {
-                        // heads 32 hs + 8 blk + 4 g + [0, 4) of accumulator registers 4 blk + [0, 4)
-                        const f32x4 wv = *(const f32x4*)&wsh[wave][u][32 * hs + 8 * blk + 4 * g];
-#pragma unroll
-                        for (int e = 0; e < 4; e++) sum = fmaf(wv[e], relu_bits(acc[4 * blk + e]), sum);
-                    }
-                }
-                sum += __shfl_xor(sum, 32, 64);
-                if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = scale * ksj * sum;
+                const float sum = fp8_head_sum<NHS>(
+                    qf[u], k0, k1, [&](int i) { return *(const f32x4*)&wsh[wave][u][i]; }, g);
+                if (g == 0 && s < n[u]) scores[(int64_t)(t0 + u) * ld + s] = fp8_score(scale, ksj, sum);
             }
             if (sub + PF < kSub) load_keys(j, sub + PF);
         }

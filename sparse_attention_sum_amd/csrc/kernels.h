@@ -24,6 +24,20 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
 // A workspace of topk_workspace_bytes() (0 when not useful) lets long rows go through two passes
 // (slices of the row, then a merge of their candidates); without it, one workgroup per row.
 size_t topk_workspace_bytes(const BatchView& bv, int k);
+// The merge pass alone: each row's selection from the slices' candidates in ws (written by the
+// first pass of launch_topk or by the fused indexer -> top-k pass), nslices slices of slice_len.
+hipError_t launch_topk_merge(const BatchView& bv, int k, void* ws, int nslices, int slice_len, int32_t* idx,
+                             hipStream_t st);
+
+// The lightning indexer fused with the top-k's first pass for long decode rows: fp8 queries and
+// keys, 32 or 64 heads, at most two queries per sequence, rows longer than 32768, pages of at least
+// 16 tokens.  indexer_topk_plan() tells whether a batch qualifies and how it is sliced (ws bytes in
+// *ws_bytes); launch_indexer_topk() then runs the fused pass and the merge, writing idx [T][k].
+bool indexer_topk_plan(int dtype, int H, const CacheView& kc, const BatchView& bv, int k, int* nslices,
+                       int* slice_len, size_t* ws_bytes);
+size_t indexer_topk_workspace_bound(const BatchView& bv, int k);   // the largest plan's bytes
+hipError_t launch_indexer_topk(const uint8_t* q, const float* q_scale, const float* w, int H, const CacheView& kc,
+                               const BatchView& bv, float scale, int k, int32_t* idx, void* ws, hipStream_t st);
 hipError_t launch_topk(const float* scores, int64_t ld, const BatchView& bv, int k, const int32_t* kq, int window,
                        int32_t* idx, void* ws, size_t ws_bytes, hipStream_t st);
 

@@ -20,11 +20,11 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 # dsa_dtype
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 # operations for dsa_workspace_size
-DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD = 0, 1, 2, 3
+DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK = 0, 1, 2, 3, 4
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_workspace_size",
            "dsa_status_string", "dsa_last_error", "dsa_version", "dsa_cache_append", "dsa_rope_queries",
-           "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc")
+           "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc", "dsa_indexer_topk")
 
 
 class DsaError(RuntimeError):
@@ -83,6 +83,7 @@ def load() -> ctypes.CDLL:
     CP, BP = ctypes.POINTER(_Cache), ctypes.POINTER(_Batch)
     L.dsa_indexer_scores.argtypes = [P, I32, P, P, I32, I32, CP, BP, F, P, I64, P]
     L.dsa_topk.argtypes = [P, I64, BP, I32, P, P, ctypes.c_size_t, P]
+    L.dsa_indexer_topk.argtypes = [P, I32, P, P, I32, I32, CP, BP, F, I32, P, P, ctypes.c_size_t, P]
     L.dsa_topk_select.argtypes = [P, I64, BP, I32, P, I32, P, P, ctypes.c_size_t, P]
     L.dsa_value_restore.argtypes = [P, P, I32, I32, I32, P, P]
     L.dsa_sparse_mla.argtypes = [P, I32, I32, I32, CP, BP, P, I32, F, P, P, P, ctypes.c_size_t, P]
@@ -98,7 +99,8 @@ def load() -> ctypes.CDLL:
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.restype = ctypes.c_char_p
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward", "dsa_cache_append",
-                 "dsa_rope_queries", "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc"):
+                 "dsa_rope_queries", "dsa_topk_select", "dsa_value_restore", "dsa_forward_noalloc",
+                 "dsa_indexer_topk"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -188,6 +190,24 @@ def dsa_indexer_scores(q: torch.Tensor, q_scale: Optional[torch.Tensor], weights
     _check(load().dsa_indexer_scores(_ptr(q), dtype_code(q), _ptr(q_scale), _ptr(weights), H, D, ctypes.byref(kc),
                                       ctypes.byref(b), float(scale), _ptr(scores), int(ld), _stream(stream)))
     return scores
+
+
+def dsa_indexer_topk(q: torch.Tensor, q_scale: Optional[torch.Tensor], weights: torch.Tensor, k_cache: Cache,
+                     batch: Batch, k: int, scale: float = 1.0, indices: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The indexer and the top-k in one call (fused for long fp8 decode rows); returns indices [T, k]
+    int32, ascending positions then -1 -- the same as dsa_topk on dsa_indexer_scores' output."""
+    T, H, D = q.shape
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        need = dsa_workspace_size(DSA_OP_INDEXER_TOPK, batch, k, H)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
+    kc, b = k_cache.struct(), batch.struct()
+    _check(load().dsa_indexer_topk(_ptr(q), dtype_code(q), _ptr(q_scale), _ptr(weights), H, D, ctypes.byref(kc),
+                                    ctypes.byref(b), float(scale), int(k), _ptr(indices), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)))
+    return indices
 
 
 def _topk_workspace(batch: Batch, k: int, workspace, device):
