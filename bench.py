@@ -233,7 +233,11 @@ def long_context_block(dev, stream, flush, timed, steps=10):
                          device=dev)
     fwd = lambda: dsa.dsa_forward(d["q_idx"], d["q_idx_scale"], d["w"], kc, k, d["q_mla"], lc, b, scale,
                                   indices_out=ind, out=out, lse=lse, workspace=ws, stream=stream)
+    it_ws = torch.empty(max(1, dsa.dsa_workspace_size(dsa.DSA_OP_INDEXER_TOPK, b, k, H)), dtype=torch.uint8,
+                        device=dev)
     stage = {
+        "indexer_topk_fused": lambda: dsa.dsa_indexer_topk(d["q_idx"], d["q_idx_scale"], d["w"], kc, b, k,
+                                                           indices=ind, workspace=it_ws, stream=stream),
         "indexer": lambda: dsa.dsa_indexer_scores(d["q_idx"], d["q_idx_scale"], d["w"], kc, b, 1.0, scores=scores,
                                                   ld=ld, stream=stream),
         "topk": lambda: dsa.dsa_topk(scores, ld, b, k, indices=ind, stream=stream, workspace=tk_ws),
@@ -246,7 +250,7 @@ def long_context_block(dev, stream, flush, timed, steps=10):
     res = {"workload": "decode-B64-ctx131072 (inputs drawn on the device)", "steps": steps,
            "ms_per_step": round(float(ms.mean()), 5), "tokens_per_s": round(T / (float(ms.mean()) / 1e3), 1),
            "stages_us": {}, "setup_s": round(gen_s, 1)}
-    for name in ("indexer", "topk", "sparse_mla"):
+    for name in ("indexer_topk_fused", "indexer", "topk", "sparse_mla"):
         stage[name]()
         sms, _ = timed(stage[name], steps)
         res["stages_us"][name] = round(float(sms.mean() * 1e3), 3)

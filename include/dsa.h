@@ -131,8 +131,11 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const dsa_batch* batch, int
  * When the rows are longer than 32768 positions, the queries are fp8 with 32 or 64 heads, a sequence
  * has at most two queries and pages (if any) hold at least 16 tokens, the scores never leave the chip:
  * each workgroup scores one slice of a sequence's positions into LDS and keeps only the slice's best k
- * as candidates, and a second pass selects each row's k from its slices' candidates.  Otherwise the
- * scores go through the workspace (queries with n_t <= k are not scored: they select every position). */
+ * as candidates, and a second pass selects each row's k from its slices' candidates; rows of at most
+ * 32768 positions (16384 with two queries per sequence) are scored and selected whole by one
+ * workgroup.  Otherwise the scores go through the workspace (queries with n_t <= k are not scored:
+ * they select every position).  The fused pass pays where its workgroups fill the GPU (e.g. 64
+ * sequences at 131072 positions); dsa_forward takes it only there. */
 dsa_status dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* weights,
                             int32_t n_heads, int32_t head_dim, const dsa_cache* k_cache, const dsa_batch* batch,
                             float scale, int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,

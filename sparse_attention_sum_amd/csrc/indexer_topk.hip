@@ -22,11 +22,14 @@ namespace {
 
 constexpr int kFuMinPage = 16;   // smallest page size taken (the slice's page table lives in LDS)
 
-template <int NHS, int QG>
+// PASS 1: the slice's best k go to the workspace as candidates (a merge pass follows).  PASS 0: the
+// slice is the whole row (n <= 32768 / QG): the selection is final and written to idx [T][k].
+template <int NHS, int QG, int PASS>
 __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ q_scale,
                                                                 const float* __restrict__ w, CacheView kc,
-                                                                BatchView bv, float scale, int k, TkSlices sl) {
+                                                                BatchView bv, float scale, int k, TkSlices sl,
+                                                                int32_t* __restrict__ idx) {
     constexpr int H = 32 * NHS;
     constexpr int PF = QG == 1 ? 6 : 4;    // subtiles in flight per wave (registers: 17 per subtile)
     // LDS: the scores of QG rows over the slice as keys, then the slice's page table
@@ -153,15 +156,22 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
             if (u > 0) __syncthreads();   // the previous row's selection is done with sh
             const uint32_t l = (QG > 1 && u > 0) ? lo[QG - 1] : lo[0];
             const uint32_t h = (QG > 1 && u > 0) ? hi[QG - 1] : hi[0];
-            topk_row<1, true>(lds + u * slen, sh, t0 + u, slice, nullptr, 0, bv, k, nullptr, 0, k, nullptr, sl, l, h);
+            topk_row<PASS, true>(lds + u * slen, sh, t0 + u, slice, nullptr, 0, bv, k, nullptr, 0, k, idx, sl, l, h);
         }
     }
 }
 
-// The fewest slices (at most 8, as the merge allows, each at most 32768 / qg keys so that its keys fit
+// Rows of at most 32768 / qg positions take one slice (the whole row, no merge).  Longer rows: the
+// fewest slices (at most 8, as the merge allows, each at most 32768 / qg keys so that its keys fit
 // LDS) that give about one workgroup per CU over the batch's sequences.
 bool plan_slices(const BatchView& bv, int k, int qg, int& ns, int& slen) {
-    if (bv.max_len <= kTwoPassMin || k <= 0 || bv.T <= 0) return false;
+    if (k <= 0 || bv.T <= 0 || bv.max_len <= k) return false;
+    if (bv.max_len * qg <= kCap) {
+        ns = 1;
+        slen = (bv.max_len + 3) & ~3;
+        return true;
+    }
+    if (bv.max_len <= kTwoPassMin) return false;
     const int cap = kCap / qg;
     const int ns_lds = (bv.max_len + cap - 1) / cap;
     const int ns_max = min(kTkWaves, kCandCap / k);
@@ -182,12 +192,12 @@ bool indexer_topk_plan(int dtype, int H, const CacheView& kc, const BatchView& b
     if (!plan_slices(bv, k, bv.max_q, ns, slen)) return false;
     *nslices = ns;
     *slice_len = slen;
-    *ws_bytes = slices_bytes(bv.T, ns, k);
+    *ws_bytes = ns > 1 ? slices_bytes(bv.T, ns, k) : 0;
     return true;
 }
 
 size_t indexer_topk_workspace_bound(const BatchView& bv, int k) {
-    if (bv.max_len <= kTwoPassMin || k <= 0 || bv.T <= 0) return 0;
+    if (bv.max_len * bv.max_q <= kCap || k <= 0 || bv.T <= 0) return 0;   // one slice: no candidates
     return slices_bytes(bv.T, min(kTkWaves, kCandCap / max(k, 1)), k);
 }
 
@@ -196,7 +206,7 @@ hipError_t launch_indexer_topk(const uint8_t* q, const float* q_scale, const flo
     int ns = 0, slen = 0;
     size_t bytes = 0;
     if (!indexer_topk_plan(DSA_FP8_E4M3, H, kc, bv, k, &ns, &slen, &bytes)) return hipErrorInvalidValue;
-    const TkSlices sl = slices_in(ws, bv.T, ns, k, slen);
+    const TkSlices sl = ns > 1 ? slices_in(ws, bv.T, ns, k, slen) : TkSlices{nullptr, nullptr, nullptr, 1, slen};
     const int qg = bv.max_q;
     const int npages = kc.page_table ? (slen + kc.page_size - 1) / kc.page_size + 1 : 0;
     const size_t shm = ((size_t)qg * slen + npages) * sizeof(uint32_t);
@@ -205,16 +215,26 @@ hipError_t launch_indexer_topk(const uint8_t* q, const float* q_scale, const flo
     auto go = [&](auto kern) {
         e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         if (e == hipSuccess) {
-            kern<<<grid, kTkBlock, shm, st>>>(q, q_scale, w, kc, bv, scale, k, sl);
+            kern<<<grid, kTkBlock, shm, st>>>(q, q_scale, w, kc, bv, scale, k, sl, idx);
             e = hipGetLastError();
         }
     };
+    if (ns == 1) {   // the whole row in one workgroup: the selection is final
+        if (qg == 1) {
+            if (H == 32) go(indexer_topk_kernel<1, 1, 0>);
+            else go(indexer_topk_kernel<2, 1, 0>);
+        } else {
+            if (H == 32) go(indexer_topk_kernel<1, 2, 0>);
+            else go(indexer_topk_kernel<2, 2, 0>);
+        }
+        return e;
+    }
     if (qg == 1) {
-        if (H == 32) go(indexer_topk_kernel<1, 1>);
-        else go(indexer_topk_kernel<2, 1>);
+        if (H == 32) go(indexer_topk_kernel<1, 1, 1>);
+        else go(indexer_topk_kernel<2, 1, 1>);
     } else {
-        if (H == 32) go(indexer_topk_kernel<1, 2>);
-        else go(indexer_topk_kernel<2, 2>);
+        if (H == 32) go(indexer_topk_kernel<1, 2, 1>);
+        else go(indexer_topk_kernel<2, 2, 1>);
     }
     if (e != hipSuccess) return e;
     return launch_topk_merge(bv, k, ws, ns, slen, idx, st);
