@@ -400,6 +400,10 @@ def main():
             print(json.dumps({"stage": "copy", "bytes_read_per_launch": 2 ** 30, "bytes_written_per_launch": 2 ** 30}))
             return
         forward()
+        if args.stage in ("topk", "sparse_mla"):
+            stage_fn("indexer")()   # the score rows the top-k stage reads (the forward keeps its own)
+            if args.stage == "sparse_mla":
+                stage_fn("topk")()
         torch.cuda.synchronize()
         fn = stage_fn(args.stage)
         for _ in range(args.warmup):

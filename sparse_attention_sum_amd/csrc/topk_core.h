@@ -248,6 +248,67 @@ __device__ __forceinline__ void compact(Key4&& key4, Pos4&& pos4, int nw, uint32
     }
 }
 
+// Ordered compaction of a working set in LDS of at most E * kTkBlock entries in one step: thread t
+// owns entries [E t, E t + E) (E / 4 16-byte reads issued together), one block-wide scan over the
+// threads' packed counts (above | equal << 16) gives each thread its first output slot and the number
+// of equal entries before its own, and the thread emits its taken entries in entry order -- equal
+// entries while fewer than need_eq precede them, so the result is the same as compact()'s.
+// nw <= E * kTkBlock <= 65535 keeps the packed sums apart.
+template <int E, typename Pos4, typename Emit>
+__device__ __forceinline__ void compact_dense(const uint32_t* keys, int nw, uint32_t mask, uint32_t thr,
+                                              uint32_t need_eq, int k, uint32_t (&wcnt)[2][kTkWaves], Pos4&& pos4,
+                                              Emit&& emit) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i0 = E * tid;
+    const int last = max(nw - 1, 0) & ~3;   // reads past the end are clamped (in bounds, not used)
+    uint32_t v[E];
+#pragma unroll
+    for (int j = 0; j < E; j += 4) {
+        const uint4 kk = *(const uint4*)(keys + min(i0 + j, last));
+        v[j] = kk.x;
+        v[j + 1] = kk.y;
+        v[j + 2] = kk.z;
+        v[j + 3] = kk.w;
+    }
+    uint32_t g = 0, e = 0;
+#pragma unroll
+    for (int j = 0; j < E; j++) {
+        const bool ok = i0 + j < nw;
+        g += (ok && (v[j] & mask) > thr) ? 1u : 0u;
+        e += (ok && (v[j] & mask) == thr) ? 1u : 0u;
+    }
+    const uint32_t own = g | (e << 16);
+    const uint32_t incl = wave_incl_scan(own);
+    if (lane == 63) wcnt[0][wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - own;
+    for (int w = 0; w < wave; w++) before += wcnt[0][w];
+    const uint32_t gt_before = before & 0xffffu;
+    uint32_t eq_seen = before >> 16;
+    uint32_t at = gt_before + min(eq_seen, need_eq);
+    if (g == 0 && (e == 0 || eq_seen >= need_eq)) return;   // nothing to take
+#pragma unroll
+    for (int j = 0; j < E; j += 4) {
+        const int4 pp = pos4(min(i0 + j, last));
+        const int p[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int x = j + jj;
+            const bool ok = i0 + x < nw;
+            const uint32_t m = v[x] & mask;
+            bool take = ok && m > thr;
+            if (ok && m == thr) {
+                take = eq_seen < need_eq;
+                eq_seen++;
+            }
+            if (take) {
+                if (at < (uint32_t)k) emit(at, p[jj], v[x]);
+                at++;
+            }
+        }
+    }
+}
+
 // Ordered compaction of a working set held in LDS of which few entries are taken (keys[i]; entry
 // i is position pos_of(i)), through bitmasks instead of per-step scans: each wave marks 64
 // consecutive entries per ballot (above the threshold / equal to it), one block-wide scan over the
@@ -636,9 +697,15 @@ __device__ __forceinline__ void topk_row(uint32_t* lds, TkShared& sh, int t, int
     // in the histogram's space, which the selection no longer needs)
     static_assert(2 * (kCap / 64) * 2 <= kHistCopies * kBins, "bitmasks must fit the histogram space");
     auto pos_of = [&](int i) -> int { return mode == kModeCand ? cpos[i] : i; };
+    // working sets in LDS: at least 8x longer than the count taken -> bitmasks; up to 16 or 32 entries
+    // per thread -> one block-wide scan; otherwise (long rows read from global memory) a scan per step
     auto compact_any = [&](int kk, auto&& emit) {
         if (mode != kModeGlobal && nw >= 8 * kk)
             compact_sparse(lds, nw, mask, thr, need_eq, kk, reinterpret_cast<uint64_t*>(&hist[0][0]), wcnt, pos_of, emit);
+        else if (mode != kModeGlobal && nw <= 16 * kTkBlock)
+            compact_dense<16>(lds, nw, mask, thr, need_eq, kk, wcnt, pos4, emit);
+        else if (mode != kModeGlobal && nw <= 32 * kTkBlock)
+            compact_dense<32>(lds, nw, mask, thr, need_eq, kk, wcnt, pos4, emit);
         else
             compact(key4, pos4, nw, mask, thr, need_eq, kk, wcnt, emit);
     };
