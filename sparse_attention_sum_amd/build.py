@@ -68,6 +68,51 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+OBJDUMP = os.path.join(os.path.dirname(BUNDLER), "llvm-objdump")
+VMEM_PREFIXES = ("global_", "buffer_", "scratch_", "flat_")
+
+
+def check_mla_prologue_wait(code_object: str) -> int:
+    """The sparse-MLA prologue awaits its index DMA with an explicit `s_waitcnt vmcnt(N)` that is
+    correct only if at least N vector-memory instructions are issued between the DMA and the wait
+    (loads complete in order, so the DMA is done once at most N of the later ones are outstanding).
+    Counted here on the assembly of this build; the build fails if the compiler emitted fewer."""
+    r = subprocess.run([OBJDUMP, "-d", "--no-show-raw-insn", code_object], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"llvm-objdump failed on {code_object}:\n{r.stderr}")
+    return mla_prologue_loads(r.stdout)
+
+
+def mla_prologue_loads(disassembly: str) -> int:
+    """Vector-memory instructions between sparse_mla_kernel's index DMA and the vmcnt wait for it, in a
+    disassembly listing; raises when they are fewer than the wait's count."""
+    lines, inside = [], False
+    for line in disassembly.splitlines():
+        if "<_ZN3dsa12_GLOBAL__N_117sparse_mla_kernel" in line:
+            inside = True
+            continue
+        if inside and line.endswith(">:"):
+            break
+        if inside:
+            lines.append(line.split("//")[0].strip())
+    dma = next((i for i, l in enumerate(lines) if l.startswith("global_load_lds_dword ")), None)
+    if dma is None:
+        raise RuntimeError("sparse_mla_kernel: index DMA (global_load_lds_dword) not found in the assembly")
+    for l in lines[dma + 1:]:
+        if l.startswith("s_waitcnt") and "vmcnt(" in l:
+            wait = l
+            break
+    else:
+        raise RuntimeError("sparse_mla_kernel: no vmcnt wait after the index DMA")
+    n = int(wait.split("vmcnt(")[1].split(")")[0])
+    end = lines.index(wait, dma + 1)
+    issued = sum(1 for l in lines[dma + 1:end] if l.split(" ")[0].startswith(VMEM_PREFIXES))
+    if issued < n:
+        raise RuntimeError(f"sparse_mla_kernel: {issued} vector-memory instructions between the index DMA and "
+                           f"'{wait}'; the wait needs at least {n} (the DMA could still be in flight)")
+    return issued
+
+
 def build(extra_flags=(), verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -79,6 +124,7 @@ def build(extra_flags=(), verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    check_mla_prologue_wait(os.path.join(BUILD, "sparse_mla.hip.co"))
     if verbose:
         print(f"built {LIB}")
     return LIB

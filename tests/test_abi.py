@@ -237,3 +237,18 @@ def test_forward_noalloc_rejects_a_batch_past_its_scratch(lib):
     assert lib.dsa_forward_noalloc(FAKE, dsa.DSA_FP8_E4M3, None, FAKE, 64, ctypes.byref(kc), 1.0, 0, FAKE, 128,
                                    ctypes.byref(lc), 1 / 24, ctypes.byref(b), None, FAKE, None,
                                    None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_mla_prologue_wait_check_counts_the_loads():
+    """build.py's check of the sparse-MLA prologue: the explicit vmcnt(18) after the index DMA is
+    sound only with at least 18 vector-memory instructions issued between them."""
+    from sparse_attention_sum_amd import build
+    head = "<_ZN3dsa12_GLOBAL__N_117sparse_mla_kernelEv>:\n\tglobal_load_lds_dword v[2:3], off\n"
+    ok = head + "\tglobal_load_dwordx4 v[4:7], v[8:9], off\n" * 18 + "\ts_waitcnt vmcnt(18)\n"
+    assert build.mla_prologue_loads(ok) == 18
+    short = head + "\tglobal_load_dwordx4 v[4:7], v[8:9], off\n" * 9 + "\ts_waitcnt vmcnt(18)\n"
+    with pytest.raises(RuntimeError):
+        build.mla_prologue_loads(short)
+    co = os.path.join(ROOT, "_build", "sparse_mla.hip.co")
+    if os.path.exists(co):
+        assert build.check_mla_prologue_wait(co) >= 18
