@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the decode-B64-ctx131072 block that the default workload's line carries")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--long-context-only", action="store_true",
+                    help="profiling aid: only the decode-B64-ctx131072 block (forward and stages, --steps each), "
+                         "printed as its own JSON line")
     ap.add_argument("--write-path", action="store_true",
                     help="measure the cache write path (query rotation + key / latent append) of the workload's "
                          "query tokens instead of the forward; prints its own JSON line")
@@ -291,6 +294,30 @@ def long_context_block(dev, stream, flush, timed, steps=10):
     return res
 
 
+def long_context_only(args, dev):
+    import torch
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def flush():
+        if not args.no_flush:
+            torch.sum(flush_buf, dim=0, keepdim=True, out=flush_out)
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in ev]), None
+
+    print(json.dumps(long_context_block(dev, stream, flush, timed, steps=args.steps)), flush=True)
+
+
 # ---------------------------------------------------------------------------------------------
 
 
@@ -310,6 +337,8 @@ def main():
     dsa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.long_context_only:
+        return long_context_only(args, dev)
     spec = WORKLOADS[args.workload](synth)
     t_gen = time.time()
     p = synth.build(spec)
