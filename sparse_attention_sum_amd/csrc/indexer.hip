@@ -14,6 +14,8 @@
 //   * bf16 prefill: four query tokens per workgroup (one per wave, 64 heads = two 32-row MFMA
 //                  tiles); 64-key tiles are staged once in LDS and shared by the four waves
 //                  (v_mfma_f32_32x32x16_bf16).  MFMA-bound.
+//   * fp8 prefill: the same streamed structure with the fp8 MFMA, for fp8 batches with more than
+//                  eight queries per sequence.
 //   * generic:     any dtype / head count, one thread per (query, key); used for fp32 inputs and
 //                  shapes the MFMA kernels do not cover.
 // The ReLU-weight-sum epilogue runs on the MFMA accumulators in registers: the 32x32 accumulator
@@ -605,6 +607,199 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
     mask_row();
 }
 
+// ---------------------------------------------------------------------------------------------
+// fp8 prefill path, streamed through LDS by DMA: the bf16 streamed kernel's structure (eight query
+// tokens per workgroup, one per wave, all heads; 64-key tiles by global_load_lds_dwordx4 into a
+// three-deep ring) with the fp8 MFMA v_mfma_f32_32x32x64_f8f6f4 (two k-steps per 128-dim key row)
+// and the per-key scale.
+//
+// Tile layout: a key row is 128 bytes = 8 chunks; DMA instruction of wave w fills bytes
+// [1024 w, +1024) of a buffer, lane L writing 16 bytes to key row kr = 8 w + L/8, slot L%8.  Slot p of
+// row r holds chunk p ^ ((r >> 1) & 7): the operand reads below (16 lanes reading one chunk of 16
+// consecutive rows) then fall in 16 distinct 16-byte bank groups (rows r and r + 8 are an even
+// number of 128-byte rows apart, so the XOR key differs between them).
+// Operand layout as in the decode kernel: in k-step ks, half g of the wave carries dims
+// 64 g + 32 ks + [0, 32) of its row (key c or head c), 32 bytes per lane per step.
+// Each tile's key scales (two per lane: keys c and 32 + c) are loaded when its DMA is issued, so a
+// tile's wait covers three vector-memory operations per lane.
+
+constexpr int kF8Tile = 64;
+constexpr int kF8TileBytes = kF8Tile * kIdxDim;   // 8 KiB
+
+template <int NHS>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void indexer_fp8_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+                               const float* __restrict__ w, CacheView kc, BatchView bv, float scale,
+                               float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
+    constexpr int H = 32 * NHS;
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_a[kF8TileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_b[kF8TileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_c[kF8TileBytes];
+    __shared__ int32_t tab[kPfTabMax];      // paged layout: first storage row of each tile, -1 if none
+    __shared__ int nmax_sh;
+
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, c = lane & 31;
+    int qb = bv.cu_q[b], qe = bv.cu_q[b + 1];
+    qb = max(0, min(qb, bv.T));
+    qe = max(qb, min(qe, bv.T));
+    const int tq0 = qb + kPfWaves * (gridDim.x - 1 - blockIdx.x);   // longest groups first
+    if (tq0 >= qe) return;
+    const int t = tq0 + wave;
+    const bool has_q = t < qe;
+    int n = has_q ? min(bv.q_len[t], bv.max_len) : 0;
+    if (n <= skip_le) n = 0;
+    n = max(n, 0);
+    if (threadIdx.x == 0) nmax_sh = 0;
+    __syncthreads();
+    if (lane == 0) atomicMax(&nmax_sh, n);
+    __syncthreads();
+    const int nmax = nmax_sh;
+    // the wave's own row past n, written after the loop (or now when no query of the block has any)
+    auto mask_row = [&]() {
+        if (mask && has_q) write_masked(scores + (int64_t)t * ld, n, ld, lane, 64);
+    };
+    if (nmax == 0) {
+        mask_row();
+        return;
+    }
+    const int ntiles = (nmax + kF8Tile - 1) / kF8Tile;
+    const bool paged = kc.page_table != nullptr;
+    if (paged) {
+        for (int j = threadIdx.x; j < ntiles; j += kPfWaves * 64) {
+            const int64_t s0 = (int64_t)j * kF8Tile;
+            const int64_t page = kc.page_table[(int64_t)b * kc.pt_stride + s0 / kc.page_size];
+            const int64_t row0 = page * kc.page_size + s0 % kc.page_size;
+            tab[j] = (page >= 0 && row0 < kc.num_rows) ? (int32_t)row0 : -1;
+        }
+    }
+
+    // operands of this wave's query: head 32 hs + c, dims 64 g + [0, 64)
+    i32x8 qf[NHS][2];
+    float wr[NHS][16];
+    const int tq = has_q ? t : tq0;
+#pragma unroll
+    for (int hs = 0; hs < NHS; hs++) {
+        const uint8_t* src = q + ((int64_t)tq * H + 32 * hs + c) * kIdxDim + 64 * g;
+        qf[hs][0] = *(const i32x8*)(src);
+        qf[hs][1] = *(const i32x8*)(src + 32);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int r = 32 * hs + 8 * (i / 4) + 4 * g + (i % 4);
+            const float sc = q_scale ? q_scale[(int64_t)tq * H + r] : 1.0f;
+            wr[hs][i] = w[(int64_t)tq * H + r] * sc;
+        }
+    }
+    if (paged) __syncthreads();   // the page table above
+    // scalar loads still outstanding in the loop would make every LDS wait there wait for all
+    asm volatile("" ::"s"(scale), "s"(ld), "s"(scores));
+    __builtin_amdgcn_s_waitcnt(0);   // operands in registers before any tile DMA is counted
+
+    // storage row of position s of tile j (-1: not a valid row)
+    auto row_of = [&](int j, int64_t s) -> int64_t {
+        if (s >= nmax) return -1;
+        if (paged) {
+            const int r0 = tab[j];
+            const int64_t row = (int64_t)r0 + (s - (int64_t)j * kF8Tile);
+            return (r0 >= 0 && row < kc.num_rows) ? row : -1;
+        }
+        return (int64_t)b * kc.seq_stride + s;
+    };
+    // DMA of tile j into buf (one instruction per wave, 8 key rows) and the tile's key scales
+    // (keys c and 32 + c of the tile, for the flush of its scores)
+    const int kr = 8 * wave + (lane >> 3);
+    float ksa[2], ksb[2], ksc[2];
+    auto issue = [&](int j, uint8_t* buf, float (&ks)[2]) {
+        const int64_t s = (int64_t)j * kF8Tile + kr;
+        const int64_t row = row_of(j, s);
+        const uint8_t* src = row >= 0 ? (const uint8_t*)kc.data + row * kIdxDim : kZeroKeyRow;
+        src += 16 * ((lane & 7) ^ ((kr >> 1) & 7));
+        pf_dma(src, lds_off(buf) + wave * 1024);
+#pragma unroll
+        for (int sub = 0; sub < 2; sub++) {
+            const int64_t rs = row_of(j, (int64_t)j * kF8Tile + 32 * sub + c);
+            const float v = kc.scale[rs >= 0 ? rs : 0];
+            ks[sub] = rs >= 0 ? v : 0.0f;
+        }
+    };
+
+    // operand read offsets: lane (g, c) takes chunks 4 g + [0, 4) of row c of a 32-key subtile
+    uint32_t roff[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) roff[i] = 128 * c + 16 * ((4 * g + i) ^ ((c >> 1) & 7));
+
+    float pend[2] = {0.0f, 0.0f};
+    int pend_s0 = -1;
+    float* srow = scores + (int64_t)t * ld;
+    auto flush = [&]() {
+        if (pend_s0 >= 0 && g == 0) {
+#pragma unroll
+            for (int sub = 0; sub < 2; sub++) {
+                const int s = pend_s0 + 32 * sub + c;
+                if (s < n) srow[s] = pend[sub];
+            }
+        }
+        pend_s0 = -1;
+    };
+
+    auto compute = [&](const uint8_t* buf, int j, const float (&ks)[2]) {
+        const int s0 = j * kF8Tile;
+        if (s0 >= n) return;
+        float sum[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int sub = 0; sub < 2; sub++) {
+            if (sub == 1 && s0 + 32 >= n) break;
+            i32x8 kf[2];
+#pragma unroll
+            for (int st = 0; st < 2; st++) {
+                const i32x4 lo = *(const i32x4*)(buf + 4096 * sub + roff[2 * st]);
+                const i32x4 hi = *(const i32x4*)(buf + 4096 * sub + roff[2 * st + 1]);
+                kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int hs = 0; hs < NHS; hs++) {
+                f32x16 acc = {};
+                acc = mfma_fp8(qf[hs][0], kf[0], acc);
+                acc = mfma_fp8(qf[hs][1], kf[1], acc);
+#pragma unroll
+                for (int i = 0; i < 16; i++) sum[sub] = fmaf(wr[hs][i], relu_bits(acc[i]), sum[sub]);
+            }
+        }
+        // the two 32-lane halves hold the two 16-head halves of every 32-head slice
+#pragma unroll
+        for (int sub = 0; sub < 2; sub++) {
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum[sub]), __float_as_uint(sum[sub]),
+                                                            false, false);
+            pend[sub] = scale * ks[sub] * (sum[sub] + __uint_as_float(h[1]));
+        }
+        pend_s0 = s0;
+    };
+
+    // tile j sits in buffer j % 3; the DMA of tile j + 2 goes to the buffer tile j - 1 used
+    auto step = [&](int j, const uint8_t* cur, const float (&kcur)[2], uint8_t* ahead, float (&kahead)[2]) {
+        if (j + 1 < ntiles)
+            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");   // this wave's part of tile j, and its scales
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        pf_barrier();                                           // everyone's part; tile j - 1 is free
+        if (j + 2 < ntiles) issue(j + 2, ahead, kahead);
+        flush();
+        compute(cur, j, kcur);
+    };
+
+    issue(0, tile_a, ksa);
+    if (ntiles > 1) issue(1, tile_b, ksb);
+    for (int j = 0; j < ntiles; j += 3) {
+        step(j, tile_a, ksa, tile_c, ksc);
+        if (j + 1 < ntiles) step(j + 1, tile_b, ksb, tile_a, ksa);
+        if (j + 2 < ntiles) step(j + 2, tile_c, ksc, tile_b, ksb);
+    }
+    flush();
+    mask_row();
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const float* w, int H,
@@ -638,6 +833,17 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
     }
     const bool stream_layout = kc.page_table == nullptr ||
                                (kc.page_size % kPfTile == 0 && (int64_t)bv.max_len <= (int64_t)kPfTabMax * kPfTile);
+    if (dtype == DSA_FP8_E4M3 && (nhs == 1 || nhs == 2) && kc.scale != nullptr && stream_layout) {
+        // fp8 with more than 8 queries per sequence: the streamed prefill kernel
+        dim3 grid((bv.max_q + kPfWaves - 1) / kPfWaves, bv.B);
+        if (nhs == 1)
+            indexer_fp8_stream_kernel<1><<<grid, kPfWaves * 64, 0, st>>>(
+                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
+        else
+            indexer_fp8_stream_kernel<2><<<grid, kPfWaves * 64, 0, st>>>(
+                (const uint8_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
+        return hipGetLastError();
+    }
     if (dtype == DSA_BF16 && (nhs == 1 || nhs == 2) && kc.scale == nullptr && stream_layout) {
         dim3 grid((bv.max_q + kPfWaves - 1) / kPfWaves, bv.B);
         if (nhs == 1)

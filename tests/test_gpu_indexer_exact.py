@@ -13,8 +13,8 @@ The score buffer is filled with NaN before each call: every entry of [n_t, ld) m
 Launch paths (the dispatch in csrc/indexer.hip): fp8 with 32 or 64 heads and at most 8 queries per
 sequence -> the fp8 decode kernel (one query per pass when max_q == 1, two otherwise); bf16 in a
 contiguous cache or 64-token pages -> the DMA-streamed kernel; bf16 in 16-token pages -> the
-four-query kernel; f32, other head counts and fp8 with more than 8 queries per sequence -> the
-generic kernel.
+four-query kernel; fp8 with more than 8 queries per sequence in a contiguous cache or 64-token pages
+-> the fp8 streamed kernel; f32 and other head counts -> the generic kernel.
 """
 import ctypes
 
@@ -42,7 +42,8 @@ CASES = [
     ("bf16-4query-h32-page16", [97, 40], [97, 3], 32, BF16, True, 16),
     ("f32-generic-h64", [600, 90], [3, 1], 64, F32, True, 64),
     ("f32-generic-h8", [257, 31], [5, 31], 8, F32, False, 64),
-    ("fp8-generic-12q-h64", [500, 77], [12, 2], 64, FP8, False, 64),
+    ("fp8-stream-12q-h64", [500, 77], [12, 2], 64, FP8, False, 64),
+    ("fp8-stream-prefill-h32-paged64", [300, 130], [300, 9], 32, FP8, True, 64),
     ("fp8-generic-h48", [700, 35], [1, 1], 48, FP8, True, 64),
 ]
 

@@ -162,7 +162,8 @@ SMALL = [
     # name, ctx, nq, idx_heads, idx dtype, k, mla heads, paged
     ("prefill-bf16-300", [300], [300], 64, synth.BF16, 64, 16, False),
     ("prefill-bf16-h32-paged", [333], [333], 32, synth.BF16, 100, 32, True),
-    ("prefill-fp8-generic", [150], [150], 64, synth.FP8, 40, 128, False),
+    ("prefill-fp8-stream", [150], [150], 64, synth.FP8, 40, 128, False),
+    ("prefill-fp8-stream-paged", [333, 70], [333, 70], 32, synth.FP8, 100, 16, True),
     ("decode-fp8-ragged", [1, 31, 32, 33, 64, 65, 100, 257, 1000, 2049, 4097], [1] * 11, 64, synth.FP8, 64, 128, True),
     ("mtp-fp8-h32", [70, 129, 3000], [2, 2, 2], 32, synth.FP8, 64, 64, False),
     ("decode-bf16-contig", [500, 1025], [1, 1], 64, synth.BF16, 128, 48, False),
@@ -229,7 +230,7 @@ def test_paged_equals_contiguous_bitwise():
 
 
 @pytest.mark.parametrize("dt,nq", [(synth.BF16, [300, 1]), (synth.FP8, [1, 1]), (synth.FP8, [300, 1])],
-                         ids=["bf16-prefill", "fp8-decode", "fp8-generic"])
+                         ids=["bf16-prefill", "fp8-decode", "fp8-prefill-stream"])
 def test_indexer_out_of_range_pages_read_as_zero_rows(dt, nq):
     """Page numbers outside [0, num_pages) read as all-zero key rows: those tokens score exactly 0
     (ReLU(0) = 0) and every other score is unchanged, bit for bit."""
