@@ -43,8 +43,10 @@ DEFAULT_WORKLOAD = "decode-B64-ctx8192"
 CPU_SAMPLE = {"tiny-prefill-L1024": 1024, "decode-B64-ctx8192": 64, "prefill-L16384": 48,
               "mtp-decode-B32x2-ctx65536-paged": 24, "ragged-decode-B16-paged": 16}
 
-KERNEL_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "sparse_mla": "sparse_mla.hip",
-                 "write_path": "cache_write.hip", "value_restore": "value_restore.hip"}
+KERNEL_SOURCE = {"indexer": ("indexer.hip", "indexer_fp8.h"), "topk": ("topk.hip", "topk_core.h"),
+                 "sparse_mla": ("sparse_mla.hip",), "write_path": ("cache_write.hip",),
+                 "value_restore": ("value_restore.hip",),
+                 "indexer_topk": ("indexer_topk.hip", "indexer_fp8.h", "topk_core.h", "topk.hip")}
 VALUE_DH = 128   # value width per head used for the value-restore measurement
 
 # Rotated spans used for the write-path measurement: the indexer key's first 64 of 128 dims, and
@@ -98,15 +100,19 @@ def algorithmic(p, stage, selected=None):
     HI, H = s.idx_heads, s.mla_heads
     long_ = n > k
     if stage == "indexer":
+        # the measured call, dsa_indexer_scores: every query scored over its n positions and every
+        # entry of its row written (-inf over [n, ld)); the forward's own indexer pass skips rows
+        # with n <= k (all their positions are selected) and the masked entries
         elt = {"f32": 4, "bf16": 2, "fp8": 1}[s.idx_dtype]
         kscale = 4 if s.idx_dtype == "fp8" else 0
-        # key cache read once per sequence (up to the longest query that needs scores)
+        ld = (int(p.max_len) + 63) // 64 * 64
+        # key cache read once per sequence (up to its longest query)
         nmax_seq = np.zeros(s.B, np.int64)
-        np.maximum.at(nmax_seq, p.q_seq, np.where(long_, n, 0))
+        np.maximum.at(nmax_seq, p.q_seq, n)
         kbytes = int(nmax_seq.sum()) * (128 * elt + kscale)
-        qbytes = int(long_.sum()) * HI * (128 * elt + 4 + (4 if s.idx_dtype == "fp8" else 0))
-        sbytes = int(n[long_].sum()) * 4
-        flops = int(n[long_].sum()) * HI * 128 * 2
+        qbytes = s.T * HI * (128 * elt + 4 + (4 if s.idx_dtype == "fp8" else 0))
+        sbytes = s.T * ld * 4
+        flops = int(n.sum()) * HI * 128 * 2
         return kbytes + qbytes + sbytes, flops
     if stage == "topk":
         if selected is not None:
@@ -139,10 +145,11 @@ def bound_of(p, stage):
 
 
 def source_hash(stage):
-    path = os.path.join(ROOT, "sparse_attention_sum_amd", "csrc", KERNEL_SOURCE[stage])
+    """sha256/16 over the stage's kernel sources, then common.h."""
+    csrc = os.path.join(ROOT, "sparse_attention_sum_amd", "csrc")
     h = hashlib.sha256()
-    for f in (path, os.path.join(ROOT, "sparse_attention_sum_amd", "csrc", "common.h")):
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SOURCE[stage] + ("common.h",):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -259,8 +266,13 @@ def long_context_block(dev, stream, flush, timed, steps=10):
         res["stages_us"][name] = round(float(sms.mean() * 1e3), 3)
     mla_bytes = T * k * (576 * 2 + 4) + T * H * (576 * 2 + 512 * 2 + 4)
     idx_bytes = T * ctx * (128 + 4) + T * 64 * (128 + 8) + T * ctx * 4
+    fused_bytes = T * ctx * (128 + 4) + T * 64 * (128 + 8) + T * k * 4
     res["sparse_mla_hbm_frac"] = round(mla_bytes / (res["stages_us"]["sparse_mla"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     res["indexer_hbm_frac"] = round(idx_bytes / (res["stages_us"]["indexer"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    res["indexer_topk_fused_hbm_frac"] = round(
+        fused_bytes / (res["stages_us"]["indexer_topk_fused"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    res["indexer_topk_fused_alg_bytes"] = fused_bytes
+    res["indexer_topk_fused_traffic"] = recorded_traffic("indexer_topk", "decode-B64-ctx131072")
     # spot check of queries 0 and 63 against the oracle (their sequences copied to the host)
     torch.cuda.synchronize()
     check = {}

@@ -24,7 +24,7 @@ def _stand_in(spec):
     """q_len / q_seq of a workload without building its tensors (each query sees its whole context)."""
     q_len = np.concatenate([np.arange(c - q + 1, c + 1) for c, q in zip(spec.ctx, spec.nq)]).astype(np.int32)
     q_seq = np.concatenate([np.full(q, b) for b, q in enumerate(spec.nq)]).astype(np.int32)
-    return types.SimpleNamespace(spec=spec, q_len=q_len, q_seq=q_seq)
+    return types.SimpleNamespace(spec=spec, q_len=q_len, q_seq=q_seq, max_len=int(max(spec.ctx)))
 
 
 def test_decode_algorithmic_work_in_closed_form():
@@ -43,13 +43,14 @@ def test_decode_algorithmic_work_in_closed_form():
     assert bench.bound_of(p, "sparse_mla") == ("hbm", None)
 
 
-def test_prefill_counts_only_rows_longer_than_k():
+def test_prefill_indexer_call_scores_every_row_and_writes_the_mask():
+    """The indexer stage is timed through dsa_indexer_scores: every causal row is scored and every
+    entry of [0, ld) written (-inf past n), so its bytes hold the whole 16384 x 16384 score matrix."""
     p = _stand_in(synth.spec_for(3))                 # one sequence, 16384 causal queries, bf16 indexer
     n = np.arange(1, 16385, dtype=np.int64)
-    long_ = n[n > 2048]
     idx_bytes, idx_flops = bench.algorithmic(p, "indexer")
-    assert idx_flops == int(long_.sum()) * 64 * 128 * 2
-    assert idx_bytes == 16384 * 256 + len(long_) * 64 * (256 + 4) + int(long_.sum()) * 4
+    assert idx_flops == int(n.sum()) * 64 * 128 * 2
+    assert idx_bytes == 16384 * 256 + 16384 * 64 * (256 + 4) + 16384 * 16384 * 4
     _, mla_flops = bench.algorithmic(p, "sparse_mla")
     assert mla_flops == int(np.minimum(n, 2048).sum()) * 128 * 1088 * 2
     assert bench.bound_of(p, "indexer") == ("mfma", "bf16")
