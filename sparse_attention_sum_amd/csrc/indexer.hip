@@ -384,6 +384,12 @@ __global__ __launch_bounds__(kPreWaves * 64) void indexer_bf16_prefill_kernel(
 // Inside a tile each wave runs 2 * NHS MFMA chains (subtile x head slice, eight MFMAs each); the
 // ReLU-weight epilogue of chain c (32 VALU instructions) is interleaved with the MFMAs of chain c + 1,
 // which keeps the VALU work in the shadow of the matrix unit.
+// With 32 heads (NHS = 1) the chains stream their key operands from LDS a few steps ahead instead of
+// holding a whole subtile's, which keeps the wave within 128 registers: two workgroups then share a
+// CU (four waves per SIMD), and each one's tile barrier and boundary work run under the other's
+// MFMAs.  At 64 heads a wave needs more than 128 registers for its query block alone plus the
+// chains, and splitting a query's heads over two waves doubles the LDS operand reads and the tile
+// DMAs per MFMA (measured slower), so that instance stays at two waves per SIMD.
 
 constexpr int kPfWaves = 8;
 constexpr int kPfTile = 64;                              // keys per tile
@@ -432,6 +438,31 @@ __device__ __forceinline__ f32x16 pf_chain(const bf16x8 (&qs)[8], const bf16x8 (
     return acc;
 }
 
+// The same chain with its key operands read from the subtile in LDS kPfAhead steps ahead (a few
+// registers instead of a subtile's 32).
+constexpr int kPfAhead = 3;
+template <bool EPI>
+__device__ __forceinline__ f32x16 pf_chain_lds(const bf16x8 (&qs)[8], const uint8_t* sub, const uint32_t (&roff)[8],
+                                               const f32x16& prev, const float (&wp)[16], float& sum) {
+    bf16x8 kb[kPfAhead];
+#pragma unroll
+    for (int u = 0; u < kPfAhead; u++) kb[u] = *(const bf16x8*)(sub + roff[u]);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) {
+        const bf16x8 k = kb[ks % kPfAhead];
+        if (ks + kPfAhead < 8) kb[ks % kPfAhead] = *(const bf16x8*)(sub + roff[ks + kPfAhead]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qs[ks], k, acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (EPI) {
+            sum = fmaf(wp[2 * ks], relu_bits(prev[2 * ks]), sum);
+            sum = fmaf(wp[2 * ks + 1], relu_bits(prev[2 * ks + 1]), sum);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ float pf_epilogue(const f32x16& a, const float (&wp)[16], float sum) {
 #pragma unroll
     for (int i = 0; i < 16; i++) sum = fmaf(wp[i], relu_bits(a[i]), sum);
@@ -439,7 +470,7 @@ __device__ __forceinline__ float pf_epilogue(const f32x16& a, const float (&wp)[
 }
 
 template <int NHS>
-__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4 / NHS, 4 / NHS)))
 void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ q_scale,
                                 const float* __restrict__ w, CacheView kc, BatchView bv, float scale,
                                 float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
@@ -557,6 +588,23 @@ void indexer_bf16_stream_kernel(const uint16_t* __restrict__ q, const float* __r
         const int s0 = j * kPfTile;
         if (s0 >= n) return;
         const bool two = s0 + 32 < n;
+        if constexpr (NHS == 1) {   // operands streamed from LDS (see above)
+            float sum0 = 0.0f, sum1 = 0.0f;
+            const f32x16 none = {};
+            f32x16 x = pf_chain_lds<false>(qf[0], buf, roff, none, wr[0], sum0);
+            if (two) {
+                x = pf_chain_lds<true>(qf[0], buf + 8192, roff, x, wr[0], sum0);
+                sum1 = pf_epilogue(x, wr[0], sum1);
+            } else {
+                sum0 = pf_epilogue(x, wr[0], sum0);
+            }
+            const auto h0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum0), __float_as_uint(sum0), false, false);
+            const auto h1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum1), __float_as_uint(sum1), false, false);
+            pend[0] = scale * (sum0 + __uint_as_float(h0[1]));
+            pend[1] = scale * (sum1 + __uint_as_float(h1[1]));
+            pend_s0 = s0;
+            return;
+        }
         bf16x8 kf0[8], kf1[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) kf0[ks] = *(const bf16x8*)(buf + roff[ks]);
