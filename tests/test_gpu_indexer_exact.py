@@ -14,7 +14,9 @@ Launch paths (the dispatch in csrc/indexer.hip): fp8 with 32 or 64 heads and at 
 sequence -> the fp8 decode kernel (one query per pass when max_q == 1, two otherwise); bf16 in a
 contiguous cache or 64-token pages -> the DMA-streamed kernel; bf16 in 16-token pages -> the
 four-query kernel; fp8 with more than 8 queries per sequence in a contiguous cache or 64-token pages
--> the fp8 streamed kernel; f32 and other head counts -> the generic kernel.
+-> the fp8 streamed kernel; f32 and other head counts -> the generic kernel.  The 32-head streamed
+kernel (operands read from LDS a few MFMAs ahead, two workgroups per CU) has a paged and a ragged
+contiguous case.
 """
 import ctypes
 
@@ -38,6 +40,7 @@ CASES = [
     ("fp8-decode-2q-h32-contig", [129, 3001], [2, 2], 32, FP8, False, 64),
     ("bf16-stream-h64-contig", [300, 1025], [300, 1], 64, BF16, False, 64),
     ("bf16-stream-h32-paged64", [333, 130], [100, 130], 32, BF16, True, 64),
+    ("bf16-stream-h32-contig-ragged", [1000, 77, 65], [37, 77, 9], 32, BF16, False, 64),
     ("bf16-4query-h64-page16", [333, 130], [100, 130], 64, BF16, True, 16),
     ("bf16-4query-h32-page16", [97, 40], [97, 3], 32, BF16, True, 16),
     ("f32-generic-h64", [600, 90], [3, 1], 64, F32, True, 64),

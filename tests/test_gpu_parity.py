@@ -162,6 +162,7 @@ SMALL = [
     # name, ctx, nq, idx_heads, idx dtype, k, mla heads, paged
     ("prefill-bf16-300", [300], [300], 64, synth.BF16, 64, 16, False),
     ("prefill-bf16-h32-paged", [333], [333], 32, synth.BF16, 100, 32, True),
+    ("prefill-bf16-h32-contig-2seq", [700, 129], [700, 65], 32, synth.BF16, 128, 16, False),
     ("prefill-fp8-stream", [150], [150], 64, synth.FP8, 40, 128, False),
     ("prefill-fp8-stream-paged", [333, 70], [333, 70], 32, synth.FP8, 100, 16, True),
     ("decode-fp8-ragged", [1, 31, 32, 33, 64, 65, 100, 257, 1000, 2049, 4097], [1] * 11, 64, synth.FP8, 64, 128, True),
