@@ -601,6 +601,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, int H, const CacheView& lat, con
         case 3: mla_combine_kernel<3><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
         case 4: mla_combine_kernel<4><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
         case 8: mla_combine_kernel<8><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        case 16: mla_combine_kernel<16><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
+        case 32: mla_combine_kernel<32><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
         default: mla_combine_kernel<0><<<blocks, kCombThreads, 0, st>>>(part_o, part_lse, splits, H, bv.T, out, lse); break;
     }
     return hipGetLastError();
