@@ -29,11 +29,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 
 WORKLOADS = {
-    "tiny-prefill-L1024": lambda s: s.spec_for(1),
-    "decode-B64-ctx8192": lambda s: s.spec_for(2),
-    "prefill-L16384": lambda s: s.spec_for(3),
-    "mtp-decode-B32x2-ctx65536-paged": lambda s: s.spec_for(4),
-    "ragged-decode-B16-paged": lambda s: s.spec_for(5),
+    "tiny-prefill-L1024": lambda s: s.named_spec("tiny-prefill-L1024"),
+    "decode-B64-ctx8192": lambda s: s.named_spec("decode-B64-ctx8192"),
+    "prefill-L16384": lambda s: s.named_spec("prefill-L16384"),
+    "mtp-decode-B32x2-ctx65536-paged": lambda s: s.named_spec("mtp-decode-B32x2-ctx65536-paged"),
+    "ragged-decode-B16-paged": lambda s: s.named_spec("ragged-decode-B16-paged"),
     "decode-B64-ctx16384": lambda s: s.sweep_spec(16384),
     "decode-B64-ctx32768": lambda s: s.sweep_spec(32768),
     "decode-B64-ctx65536": lambda s: s.sweep_spec(65536),

@@ -227,23 +227,26 @@ def ragged_lengths(rng, B=16, lo=1000, hi=131072, n_short=3, short_hi=2048) -> L
     return [int(round(v)) for v in lens]
 
 
-def spec_for(config: int) -> Spec:
-    """Workloads 1..5 (tiny prefill, batched decode, long prefill, two-token decode, ragged)."""
-    if config == 1:
-        return Spec("tiny-prefill-L1024", ctx=[1024], nq=[1024], idx_heads=4, idx_dtype=F32,
-                    topk=256, mla_heads=8, seed=0)
-    if config == 2:
-        return Spec("decode-B64-ctx8192", ctx=[8192] * 64, nq=[1] * 64, idx_dtype=FP8, seed=1)
-    if config == 3:
-        return Spec("prefill-L16384", ctx=[16384], nq=[16384], idx_dtype=BF16, seed=2)
-    if config == 4:
-        return Spec("mtp-decode-B32x2-ctx65536-paged", ctx=[65536] * 32, nq=[2] * 32,
-                    idx_dtype=FP8, paged=True, seed=3)
-    if config == 5:
+def named_spec(name: str) -> Spec:
+    """The five workloads by name: tiny causal prefill (L = 1024, fp32 indexer, 4 heads), batched decode
+    (64 x 8192, fp8), long causal prefill (L = 16384, bf16), two-token decode (32 x 2 at 65536, paged),
+    and ragged long-context decode (16 sequences, paged)."""
+    if name == "tiny-prefill-L1024":
+        return Spec(name, ctx=[1024], nq=[1024], idx_heads=4, idx_dtype=F32, topk=256, mla_heads=8, seed=0)
+    if name == "decode-B64-ctx8192":
+        return Spec(name, ctx=[8192] * 64, nq=[1] * 64, idx_dtype=FP8, seed=1)
+    if name == "prefill-L16384":
+        return Spec(name, ctx=[16384], nq=[16384], idx_dtype=BF16, seed=2)
+    if name == "mtp-decode-B32x2-ctx65536-paged":
+        return Spec(name, ctx=[65536] * 32, nq=[2] * 32, idx_dtype=FP8, paged=True, seed=3)
+    if name == "ragged-decode-B16-paged":
         rng = np.random.default_rng(4 + 1000)   # lengths from their own stream, seeded by the workload
-        return Spec("ragged-decode-B16-paged", ctx=ragged_lengths(rng), nq=[1] * 16,
-                    idx_dtype=FP8, paged=True, seed=4)
-    raise ValueError(config)
+        return Spec(name, ctx=ragged_lengths(rng), nq=[1] * 16, idx_dtype=FP8, paged=True, seed=4)
+    raise ValueError(name)
+
+
+NAMED = ("tiny-prefill-L1024", "decode-B64-ctx8192", "prefill-L16384", "mtp-decode-B32x2-ctx65536-paged",
+         "ragged-decode-B16-paged")
 
 
 def sweep_spec(ctx: int, batch: int = 64) -> Spec:
@@ -296,9 +299,9 @@ def peaked_spec() -> Spec:
     """Tiny-prefill shapes with MLA q ~ N(0, 72^2): with latent ~ N(0, 1/24^2) and the 1/sqrt(576)
     softmax scale, each logit then has standard deviation 72 * 24 / 24 / 24 = 3, so the softmax is
     far from uniform and the running-max rescaling is exercised."""
-    s = spec_for(1)
+    s = named_spec("tiny-prefill-L1024")
     return dataclasses.replace(s, name="tiny-prefill-peaked", mla_q_sigma=72.0)
 
 
-__all__ = ["Spec", "Problem", "build", "spec_for", "sweep_spec", "peaked_spec", "ragged_lengths", "small_integer_indexer",
+__all__ = ["Spec", "Problem", "build", "named_spec", "NAMED", "sweep_spec", "peaked_spec", "ragged_lengths", "small_integer_indexer",
            "F32", "BF16", "FP8", "D_INDEX", "D_QK", "D_V", "PAGE"]

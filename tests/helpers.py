@@ -74,7 +74,7 @@ def recall(gpu_idx, want_idx):
 
 
 def check_mla(out_gpu, lse_gpu, out_ref, lse_ref, label=""):
-    """Spec bars (max-abs 2e-2, mean-abs 5e-3) plus relative-RMS 1e-2 (whole) / 2e-2 (per row)
+    """The stated bars (max-abs 2e-2, mean-abs 5e-3) plus relative-RMS 1e-2 (whole) / 2e-2 (per row)
     and |dlse| <= 1e-3."""
     g = out_gpu.astype(np.float64)
     d = np.abs(g - out_ref)

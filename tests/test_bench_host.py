@@ -28,7 +28,7 @@ def _stand_in(spec):
 
 
 def test_decode_algorithmic_work_in_closed_form():
-    p = _stand_in(synth.spec_for(2))                 # 64 sequences x 8192, one query each, fp8 indexer
+    p = _stand_in(synth.named_spec("decode-B64-ctx8192"))                 # 64 sequences x 8192, one query each, fp8 indexer
     T, n, HI, H, k = 64, 8192, 64, 128, 2048
     idx_bytes, idx_flops = bench.algorithmic(p, "indexer")
     # keys (128 fp8 + 4-byte scale) once per sequence, q (fp8 + weight + q scale) per head, f32 scores
@@ -46,7 +46,7 @@ def test_decode_algorithmic_work_in_closed_form():
 def test_prefill_indexer_call_scores_every_row_and_writes_the_mask():
     """The indexer stage is timed through dsa_indexer_scores: every causal row is scored and every
     entry of [0, ld) written (-inf past n), so its bytes hold the whole 16384 x 16384 score matrix."""
-    p = _stand_in(synth.spec_for(3))                 # one sequence, 16384 causal queries, bf16 indexer
+    p = _stand_in(synth.named_spec("prefill-L16384"))                 # one sequence, 16384 causal queries, bf16 indexer
     n = np.arange(1, 16385, dtype=np.int64)
     idx_bytes, idx_flops = bench.algorithmic(p, "indexer")
     assert idx_flops == int(n.sum()) * 64 * 128 * 2

@@ -111,27 +111,27 @@ def _sample(T, q_len, k, extra=(), n=8, seed=0):
     return sorted(rows)
 
 
-def test_config1_tiny_prefill_all_rows():
-    dp = device_problem(synth.spec_for(1))
+def test_tiny_prefill_L1024_all_rows():
+    dp = device_problem(synth.named_spec("tiny-prefill-L1024"))
     T = dp.spec.T
     check_problem(dp, range(T), range(T), range(0, T, 7), "tiny prefill")
 
 
-def test_config1_peaked_softmax():
+def test_tiny_prefill_L1024_peaked_softmax():
     dp = device_problem(synth.peaked_spec())
     T = dp.spec.T
     check_problem(dp, range(0, T, 97), range(T), range(0, T, 5), "peaked")
 
 
-def test_config2_batched_decode():
-    dp = device_problem(synth.spec_for(2))
+def test_decode_B64_ctx8192():
+    dp = device_problem(synth.named_spec("decode-B64-ctx8192"))
     p = dp.problem
     rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=(0, 63))
     check_problem(dp, rows, range(p.spec.T), rows, "decode B64 8K")
 
 
-def test_config3_long_prefill_sampled():
-    dp = device_problem(synth.spec_for(3))
+def test_prefill_L16384_sampled():
+    dp = device_problem(synth.named_spec("prefill-L16384"))
     p = dp.problem
     edge = (0, 1, 2046, 2047, 2048, 2049, 4095, 16383)
     rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=edge, n=6, seed=3)
@@ -139,15 +139,15 @@ def test_config3_long_prefill_sampled():
     check_problem(dp, rows, topk_rows, rows, "prefill 16K")
 
 
-def test_config4_mtp_paged_decode():
-    dp = device_problem(synth.spec_for(4))
+def test_mtp_decode_B32x2_ctx65536_paged():
+    dp = device_problem(synth.named_spec("mtp-decode-B32x2-ctx65536-paged"))
     p = dp.problem
     rows = _sample(p.spec.T, p.q_len, p.spec.topk, extra=(0, 1, 62, 63), n=4, seed=4)
     check_problem(dp, rows, range(p.spec.T), rows, "MTP decode paged 64K")
 
 
-def test_config5_ragged_paged_decode():
-    dp = device_problem(synth.spec_for(5))
+def test_ragged_decode_B16_paged():
+    dp = device_problem(synth.named_spec("ragged-decode-B16-paged"))
     p = dp.problem
     assert (p.q_len <= 2048).sum() >= 3
     T = p.spec.T
@@ -263,7 +263,7 @@ def test_indexer_out_of_range_pages_read_as_zero_rows(dt, nq):
 
 
 def test_deterministic_repeat():
-    spec = synth.spec_for(5)
+    spec = synth.named_spec("ragged-decode-B16-paged")
     dp = device_problem(spec)
     a = run_chain(dp, spec.topk)
     b = run_chain(dp, spec.topk)

@@ -78,7 +78,7 @@ def test_topk_select_plain_equals_topk():
 def test_window_selection_feeds_sparse_mla():
     """decode 64 x 8192: indexer scores -> per-query k and a 256-token window -> sparse MLA over
     k + 256 slots; the output equals the oracle's attention over the same index lists."""
-    spec = synth.spec_for(2)
+    spec = synth.named_spec("decode-B64-ctx8192")
     log(f"case: {spec.name} window selection -> sparse MLA")
     p = synth.build(spec)
     dp = to_device(p)
