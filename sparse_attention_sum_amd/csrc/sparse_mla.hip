@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bool wave_on = kHeadsPerGroup * hg < H;
 
     // Memory order of the prologue: the first pass of index reads, then the query half-block, then
-    // (after the compaction) the first two tile gathers.  The compaction synchronises through LDS
+    // (after the compaction) the first tile's gathers; the second tile's follow the first barrier,
+    // so that they do not join the prologue's burst of reads from every workgroup at once.  The compaction synchronises through LDS
     // only, so the query loads -- 18 per lane, each spanning 32 head rows -- stay in flight while
     // it runs.
     // The first 512 index entries go straight into LDS (tile_c is unused until the loop) with a
@@ -212,7 +213,6 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         }
     };
     if (ntiles > 0) load_tile(0, tile_a);
-    if (ntiles > 1) load_tile(1, tile_b);
     qlast[wave][lane] = q_last;   // waits for the query loads only; the gathers stay in flight
     const uint32_t qlast_addr = lds_addr(&qlast[wave][lane]);
 
@@ -378,8 +378,9 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         pv_tile(oacc, tb, z, m_run);
     };
 
-    wait_ahead(true, ntiles > 1);
+    wait_ahead(true, false);
     lds_barrier();
+    if (ntiles > 1) load_tile(1, tile_b);   // under tile 0's work rather than in the prologue's burst
     for (int tile = 0; tile < ntiles; tile += 3) {
         // tile i is consumed while tiles i+1 (issued earlier) and i+2 (issued during tile i) are
         // in flight
