@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
                                                                 BatchView bv, float scale, int k, TkSlices sl,
                                                                 int32_t* __restrict__ idx) {
     constexpr int H = 32 * NHS;
-    constexpr int PF = QG == 1 ? 6 : 4;    // subtiles in flight per wave (registers: 17 per subtile)
+    constexpr int PF = QG == 1 ? 6 : 3;    // subtiles in flight per wave (registers: 17 per subtile)
     // LDS: the scores of QG rows over the slice as keys, then the slice's page table
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ TkShared sh;
@@ -135,10 +135,22 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
                     const i32x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
                     const i32x8 k0 = ok ? kf[j][0] : zero, k1 = ok ? kf[j][1] : zero;
                     const float ksj = ok ? ks[j] : 0.0f;
+                    // With two queries the weights' LDS address passes through an empty asm at every
+                    // subtile, so that the compiler does not hoist the weight reads out of the loop:
+                    // held, they took 32 registers per query and the two-query kernel spilled (the
+                    // values, and so the scores, are the same either way).  One query keeps them held.
+                    uint32_t wbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&wsh[0][0];
+                    if constexpr (QG > 1) asm volatile("" : "+v"(wbase));
 #pragma unroll
                     for (int u = 0; u < QG; u++) {
                         const float sum = fp8_head_sum<NHS>(
-                            qf[u], k0, k1, [&](int i) { return *(const f32x4*)&wsh[u][i]; }, g);
+                            qf[u], k0, k1,
+                            [&](int i) {
+                                if constexpr (QG == 1) return *(const f32x4*)&wsh[u][i];
+                                typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+                                return *(lds_f32x4*)(uintptr_t)(wbase + 4u * (uint32_t)(u * H + i));
+                            },
+                            g);
                         if (g == 0 && i0 + j < nmy && pos < nrow[u]) {
                             const uint32_t key = order_key(fp8_score(scale, ksj, sum));
                             lds[u * slen + pos] = key;
