@@ -180,15 +180,17 @@ size_t indexer_topk_bytes(const dsa_batch* batch, int32_t k) {
 }
 
 // The forward takes the fused indexer -> top-k pass where it measured faster than the unfused one:
-// slices that give a workgroup to every CU, with one or two queries per sequence.  (Measured, indexer
-// + top-k: 64 x 131072 229 us fused against 275 us; 64 x 65536 129 against 148; two queries per
-// sequence at 32 x 65536 104 against 120 paged, 100 against 109 contiguous; but 16 x 131072 117
-// against 100: fewer workgroups leave CUs idle that the unfused indexer keeps busy.)
+// rows longer than one slice, over slices that give a workgroup to every CU, with one or two queries
+// per sequence.  (Measured, indexer + top-k: 64 x 131072 229 us fused against 275 us; 64 x 65536 129
+// against 148; two queries per sequence at 32 x 65536 104 against 120 paged, 100 against 109
+// contiguous; but 16 x 131072 117 against 100: fewer workgroups leave CUs idle that the unfused
+// indexer keeps busy.  Rows that fit one slice, split into four at 64 x 32768: the merge of the
+// slices' 8192 candidates per row, 14 us, takes back what the fused scoring saves inside the forward.)
 bool forward_fuses(int32_t q_idx_dtype, int32_t idx_heads, const dsa_cache* k_cache, const dsa_batch* batch,
                    int32_t k) {
     int ns = 0, slen = 0;
     size_t bytes = 0;
-    if (batch->max_q > 2) return false;
+    if (batch->max_q > 2 || !dsa::indexer_topk_rows_exceed_slice(view(batch))) return false;
     if (!dsa::indexer_topk_plan(q_idx_dtype, idx_heads, view(k_cache), view(batch), k, &ns, &slen, &bytes))
         return false;
     return (int64_t)batch->num_seqs * ns >= 256;

@@ -21,6 +21,7 @@ namespace dsa {
 namespace {
 
 constexpr int kFuMinPage = 16;   // smallest page size taken (the slice's page table lives in LDS)
+constexpr int kFuSplitMin = 8192;   // a row that fits one slice is split only into slices this long
 
 // PASS 1: the slice's best k go to the workspace as candidates (a merge pass follows).  PASS 0: the
 // slice is the whole row (n <= 32768 / QG): the selection is final and written to idx [T][k].
@@ -173,14 +174,21 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
     }
 }
 
-// Rows of at most 32768 / qg positions take one slice (the whole row, no merge).  Longer rows: the
-// fewest slices (at most 8, as the merge allows, each at most 32768 / qg keys so that its keys fit
-// LDS) that give about one workgroup per CU over the batch's sequences.
+// Rows of at most 32768 / qg positions take one slice (the whole row, no merge), or, when that leaves
+// CUs idle, slices of at least kFuSplitMin positions.  Longer rows: the fewest slices (at most 8, as
+// the merge allows, each at most 32768 / qg keys so that its keys fit LDS) that give about one
+// workgroup per CU over the batch's sequences.
 bool plan_slices(const BatchView& bv, int k, int qg, int& ns, int& slen) {
     if (k <= 0 || bv.T <= 0 || bv.max_len <= k) return false;
     if (bv.max_len * qg <= kCap) {
-        ns = 1;
-        slen = (bv.max_len + 3) & ~3;
+        // the row fits one slice; when one workgroup per sequence would leave CUs idle, it is split
+        // into slices of at least kFuSplitMin positions (measured: 64 x 32768 as four slices of 8192,
+        // indexer + top-k 81 us against 87 unfused and 150 as one slice; slices of 4096 lost to the
+        // unfused pair, their merge outweighing the extra workgroups)
+        const int ns_fill = (256 + bv.B - 1) / bv.B;
+        const int nsp = min(min(ns_fill, min(kTkWaves, kCandCap / k)), bv.max_len / kFuSplitMin);
+        ns = nsp >= 2 ? nsp : 1;
+        slen = ((bv.max_len + ns - 1) / ns + 3) & ~3;
         return true;
     }
     if (bv.max_len <= kTwoPassMin) return false;
@@ -208,8 +216,11 @@ bool indexer_topk_plan(int dtype, int H, const CacheView& kc, const BatchView& b
     return true;
 }
 
+bool indexer_topk_rows_exceed_slice(const BatchView& bv) { return (int64_t)bv.max_len * bv.max_q > kCap; }
+
 size_t indexer_topk_workspace_bound(const BatchView& bv, int k) {
-    if (bv.max_len * bv.max_q <= kCap || k <= 0 || bv.T <= 0) return 0;   // one slice: no candidates
+    if (k <= 0 || bv.T <= 0) return 0;
+    if (bv.max_len * bv.max_q <= kCap && bv.max_len < 2 * kFuSplitMin) return 0;   // one slice: no candidates
     return slices_bytes(bv.T, min(kTkWaves, kCandCap / max(k, 1)), k);
 }
 

@@ -35,6 +35,8 @@ hipError_t launch_topk_merge(const BatchView& bv, int k, void* ws, int nslices, 
 // *ws_bytes); launch_indexer_topk() then runs the fused pass and the merge, writing idx [T][k].
 bool indexer_topk_plan(int dtype, int H, const CacheView& kc, const BatchView& bv, int k, int* nslices,
                        int* slice_len, size_t* ws_bytes);
+// true when the batch's rows are longer than one fused slice holds (a merge pass is needed anyway)
+bool indexer_topk_rows_exceed_slice(const BatchView& bv);
 size_t indexer_topk_workspace_bound(const BatchView& bv, int k);   // the largest plan's bytes
 hipError_t launch_indexer_topk(const uint8_t* q, const float* q_scale, const float* w, int H, const CacheView& kc,
                                const BatchView& bv, float scale, int k, int32_t* idx, void* ws, hipStream_t st);

@@ -5,9 +5,10 @@ against the oracle directly.
 
 Cases cover one and two queries per sequence, contiguous caches and pages of 64 and 16 tokens, rows
 shorter than k (every position selected), rows that end inside a slice or a 32-key subtile, sequences
-shorter than a slice, rows short enough for one workgroup to select them whole (no merge pass), and
-shapes that do not qualify for the fused pass (bf16, 48 heads), which take the scores through the
-workspace instead.
+shorter than a slice, rows short enough for one workgroup to select them whole (no merge pass), rows
+that fit one workgroup but are split into slices of at least 8192 positions because one workgroup
+per sequence would leave CUs idle, and shapes that do not qualify for the fused pass (bf16, 48
+heads), which take the scores through the workspace instead.
 """
 import numpy as np
 import pytest
@@ -26,9 +27,11 @@ CASES = [
     ("fused-2q-paged64", [70000, 65537, 50000], [2, 2, 1], 64, synth.FP8, True, 64),
     ("fused-1q-h32-page16-short-rows", [40000, 2000, 33000, 1500, 90000], [1] * 5, 32, synth.FP8, True, 16),
     ("fused-2q-h32-contig", [36000, 33333], [2, 2], 32, synth.FP8, False, 64),
-    ("row-1q-contig", [8192] * 4 + [3000, 20000], [1] * 6, 64, synth.FP8, False, 64),
+    ("row-1q-contig", [8192] * 4 + [3000, 8000], [1] * 6, 64, synth.FP8, False, 64),
+    ("split-1q-contig-mid", [20000, 17000, 3000, 32768], [1] * 4, 64, synth.FP8, False, 64),
+    ("split-1q-paged64-mid", [24576, 16385, 900], [1] * 3, 64, synth.FP8, True, 64),
     ("row-2q-paged64", [16000, 9000, 500], [2, 2, 1], 64, synth.FP8, True, 64),
-    ("row-1q-h32-page16", [32768, 2049, 2048, 100], [1] * 4, 32, synth.FP8, True, 16),
+    ("split-1q-h32-page16", [32768, 2049, 2048, 100], [1] * 4, 32, synth.FP8, True, 16),
     ("unfused-bf16", [40000, 9000], [1, 1], 64, synth.BF16, False, 64),
     ("unfused-h48", [50000, 700], [1, 1], 48, synth.FP8, True, 64),
 ]
