@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar addresses
     const uint32_t flag_mine = lds_addr(&xflag[wave_s]), flag_other = lds_addr(&xflag[wave_s ^ 1]);
     int xepoch = 0;
-    auto logits = [&](int tile, f32x16& z) -> float {   // z: this wave's partial logits in, full logits out
+    auto publish = [&](const f32x16& z) {
         // z comes straight from the MFMA chain; the hazard padding the compiler adds before its own
         // reads of an MFMA result is not applied to inline asm, so the block starts with 20 wait
         // states itself (more than any MFMA result needs before an LDS instruction reads it).
@@ -286,6 +286,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
             "v"(f32x4{z[8], z[9], z[10], z[11]}), "v"(f32x4{z[12], z[13], z[14], z[15]}), "v"(flag_mine),
             "v"(xepoch + 1) : "memory");
         xepoch++;
+    };
+    auto logits = [&](int tile, f32x16& z) -> float {   // z: this wave's partial logits in, full logits out
         // bounded wait for the partner (both waves of a pair run the same sequence of exchanges,
         // so the count always arrives; the bound only keeps a broken invariant from hanging)
         for (int spin = 0; spin < (1 << 22); spin++) {
@@ -366,8 +368,12 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // keep the scheduler from stretching register lifetimes across it.  Tile i + 2 is gathered
         // into the buffer that tile i - 1 freed once this wave's QK step is issued: waves reach this
         // point at different times, so the workgroup's gathers do not all queue at the barrier.
+        // The partial logits are published before those gathers are issued, so the partner finds
+        // them when it is done with its own (about 1 us less per launch than publishing after).
         __builtin_amdgcn_sched_barrier(0);
         f32x16 z = qk_tile(tb);
+        __builtin_amdgcn_sched_barrier(0);
+        publish(z);
         __builtin_amdgcn_sched_barrier(0);
         if (tile + 2 < ntiles) load_tile(tile + 2, nb);
         __builtin_amdgcn_sched_barrier(0);
@@ -451,6 +457,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         f32x16 z = wave_on ? qk_tile(tile_a) : f32x16{};
+        publish(z);
         m_exact = fmaxf(m_exact, logits(tile, z));
     }
     f32x16 acc2[kVHalf / 32];
@@ -463,6 +470,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         f32x16 z = wave_on ? qk_tile(tile_a) : f32x16{};
+        publish(z);
         logits(tile, z);
         if (wave_on) pv_tile(acc2, tile_a, z, m_exact);
     }
