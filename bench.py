@@ -260,6 +260,7 @@ def long_context_block(dev, stream, flush, timed, steps=10):
     res = {"workload": "decode-B64-ctx131072 (inputs drawn on the device)", "steps": steps,
            "ms_per_step": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
            "tokens_per_s": round(T / (float(ms.mean()) / 1e3), 1),
+           "step_ms": [round(float(x), 4) for x in ms],
            "stages_us": {}, "setup_s": round(gen_s, 1)}
     for name in ("indexer_topk_fused", "indexer", "topk", "sparse_mla"):
         stage[name]()
