@@ -124,6 +124,33 @@ def test_forward_validation(lib):
     assert st == dsa.DSA_ERR_UNSUPPORTED                     # indexer q / cache dtype mismatch
 
 
+def _itk(lib, k=2048, indices=FAKE, head_dim=128, batch=None, cache=None, ws=None, ws_bytes=0):
+    b = batch or _batch()
+    c = cache or _cache()
+    return lib.dsa_indexer_topk(FAKE, dsa.DSA_FP8_E4M3, None, FAKE, 64, head_dim, ctypes.byref(c), ctypes.byref(b),
+                                1.0, k, indices, ws, ws_bytes, None)
+
+
+def test_indexer_topk_validation(lib):
+    assert _itk(lib, k=0) == dsa.DSA_ERR_INVALID_ARG
+    assert _itk(lib, k=70000) == dsa.DSA_ERR_INVALID_ARG
+    assert _itk(lib, indices=None) == dsa.DSA_ERR_INVALID_ARG
+    assert _itk(lib, head_dim=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert _itk(lib, batch=_batch(T=0)) == dsa.DSA_OK                       # empty batch: nothing launched
+    # long fp8 decode rows take the fused route, which keeps the slices' candidates in the workspace
+    long_b = _batch(T=64, B=64, max_len=131072, max_q=1)
+    long_c = _cache(rows=64 * 131072, stride=131072)
+    need = lib.dsa_workspace_size(dsa.DSA_OP_INDEXER_TOPK, ctypes.byref(long_b), 2048, 64, 512)
+    assert need > 0
+    assert _itk(lib, batch=long_b, cache=long_c) == dsa.DSA_ERR_WORKSPACE
+    assert b"workspace" in lib.dsa_last_error()
+    assert _itk(lib, batch=long_b, cache=long_c, ws=FAKE, ws_bytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    # rows longer than k on the unfused route need the score rows in the workspace
+    mid_b = _batch(T=4, B=1, max_len=5000, max_q=4)
+    mid_c = _cache(rows=5000, stride=5000)
+    assert _itk(lib, batch=mid_b, cache=mid_c) == dsa.DSA_ERR_WORKSPACE
+
+
 def test_workspace_sizes(lib):
     # decode: 64 queries, k = 2048 -> 4 splits of 512 slots
     b = _batch(T=64, B=64, max_len=8192, max_q=1)
