@@ -144,7 +144,7 @@ def test_indexer_topk_validation(lib):
     assert need > 0
     assert _itk(lib, batch=long_b, cache=long_c) == dsa.DSA_ERR_WORKSPACE
     assert b"workspace" in lib.dsa_last_error()
-    assert _itk(lib, batch=long_b, cache=long_c, ws=FAKE, ws_bytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert _itk(lib, batch=long_b, cache=long_c, ws=FAKE, ws_bytes=16) == dsa.DSA_ERR_WORKSPACE
     # rows longer than k on the unfused route need the score rows in the workspace
     mid_b = _batch(T=4, B=1, max_len=5000, max_q=4)
     mid_c = _cache(rows=5000, stride=5000)
