@@ -254,8 +254,10 @@ def long_context_block(dev, stream, flush, timed, steps=10):
         "sparse_mla": lambda: dsa.dsa_sparse_mla(d["q_mla"], lc, b, ind, scale, out=out, lse=lse, workspace=mla_ws,
                                                  stream=stream),
     }
-    for _ in range(3):
+    for _ in range(3):   # warm-up steps shaped like the timed ones (flush, then the forward)
+        flush()
         fwd()
+    torch.cuda.synchronize()
     ms, _ = timed(fwd, steps)
     res = {"workload": "decode-B64-ctx131072 (inputs drawn on the device)", "steps": steps,
            "ms_per_step": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
