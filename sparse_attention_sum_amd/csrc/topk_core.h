@@ -717,6 +717,26 @@ __device__ __forceinline__ void topk_row(uint32_t* lds, TkShared& sh, int t, int
         if (tid == 0) sl.ccnt[(int64_t)t * sl.nslices + slice] = kts;
         return;
     }
+    // no window, a dense working set in LDS and a 16-byte aligned row: the selection is staged in
+    // the histogram space (free now; the dense compaction does not use it) and written with one
+    // 16-byte store per four entries, instead of a 4-byte store per entry from the compaction's
+    // threads (top-k at decode 64 x 8192 13.1 -> 12.5 us)
+    if (wn == 0 && mode != kModeGlobal && nw < 8 * kt && nw <= 32 * kTkBlock && kt <= kHistCopies * kBins &&
+        (reinterpret_cast<uintptr_t>(orow) & 15) == 0) {
+        int32_t* stage = reinterpret_cast<int32_t*>(&hist[0][0]);
+        auto put = [&](uint32_t at, int pos, uint32_t) { stage[at] = pos; };
+        if (nw <= 16 * kTkBlock)
+            compact_dense<16>(lds, nw, mask, thr, need_eq, kt, wcnt, pos4, put);
+        else
+            compact_dense<32>(lds, nw, mask, thr, need_eq, kt, wcnt, pos4, put);
+        __syncthreads();
+        for (int i = 4 * tid; i < kt; i += 4 * kTkBlock) {
+            if (i + 3 < kt) *(int4*)(orow + i) = *(const int4*)(stage + i);
+            else for (int j = i; j < kt; j++) orow[j] = stage[j];
+        }
+        for (int i = kt + tid; i < width; i += kTkBlock) orow[i] = -1;
+        return;
+    }
     if (tid == 0) first_win = (uint32_t)kt;   // ordered before compact's writes by its barrier
     // positions in the window [wlo, n) are written with the window block; the first of them marks
     // where that block starts
