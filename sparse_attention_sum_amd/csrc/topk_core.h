@@ -634,7 +634,7 @@ __device__ __forceinline__ void topk_row(uint32_t* lds, TkShared& sh, int t, int
             const int width = min(kDigitBits, pos + 1);
             const int shift = pos + 1 - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < kHistCopies * kBins; i += kTkBlock) (&hist[0][0])[i] = 0u;
+            for (int i = 4 * tid; i < kHistCopies * kBins; i += 4 * kTkBlock) *(uint4*)(&hist[0][0] + i) = uint4{0u, 0u, 0u, 0u};
             __syncthreads();
             uint32_t* myhist = hist[wave % kHistCopies];
             auto count = [&](int, uint32_t kk) {
@@ -647,14 +647,15 @@ __device__ __forceinline__ void topk_row(uint32_t* lds, TkShared& sh, int t, int
                 // the digit d with (count above d) < remaining <= (count at or above d): thread t
                 // owns bins [4t, 4t + 4); a suffix scan over the block gives the keys above them
                 constexpr int kPerThread = kBins / kTkBlock;
+                static_assert(kPerThread == 4 && kHistCopies == 2, "a thread's bins: one 16-byte read per copy");
                 uint32_t c[kPerThread], local = 0u;
-#pragma unroll
-                for (int j = 0; j < kPerThread; j++) {
-                    c[j] = 0u;
-#pragma unroll
-                    for (int h = 0; h < kHistCopies; h++) c[j] += hist[h][kPerThread * tid + j];
-                    local += c[j];
-                }
+                const uint4 c0 = *(const uint4*)&hist[0][kPerThread * tid];
+                const uint4 c1 = *(const uint4*)&hist[1][kPerThread * tid];
+                c[0] = c0.x + c1.x;
+                c[1] = c0.y + c1.y;
+                c[2] = c0.z + c1.z;
+                c[3] = c0.w + c1.w;
+                local = (c[0] + c[1]) + (c[2] + c[3]);
                 const uint32_t incl = wave_incl_scan(local);
                 const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
                 const uint32_t suf = wtot - incl + local;  // sum over this wave's lanes >= lane
