@@ -22,8 +22,11 @@
 //
 // Rows longer than kTwoPassMin, given a workspace, take two passes instead: slices of the row, one
 // workgroup each, keep their own best k as candidates, and one workgroup per row selects from their
-// union (see TkSlices).  A working set of which at most an eighth is taken is compacted through
-// bitmasks (compact_sparse), denser ones with a scan per 256 entries (compact).
+// union (see TkSlices).  A working set in LDS of which at most an eighth is taken is compacted
+// through bitmasks (compact_sparse), a denser one of up to 32 entries per thread in one block-wide
+// scan (compact_dense; the final selection of a row without a window is then staged in LDS and
+// written with 16-byte stores), and a row read from global memory with a scan per 256 entries
+// (compact).
 #pragma once
 
 #include "kernels.h"
