@@ -322,6 +322,9 @@ def long_context_only(args, dev):
 
     def timed(fn, reps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
+            e0.record(stream)
+            e1.record(stream)
         torch.cuda.synchronize()
         for e0, e1 in ev:
             flush()
@@ -422,6 +425,9 @@ def main():
 
     def timed(fn, reps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
+            e0.record(stream)
+            e1.record(stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1 in ev:
@@ -603,6 +609,9 @@ def value_restore_bench(args, spec, p, dev, stream):
     for _ in range(args.warmup):
         step()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
+        e0.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     for e0, e1 in ev:
         if not args.no_flush:
@@ -694,6 +703,9 @@ def write_path_bench(args, spec, p, dp, dev, stream):
     for _ in range(args.warmup):
         step()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
+        e0.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     for e0, e1 in ev:
         if not args.no_flush:
