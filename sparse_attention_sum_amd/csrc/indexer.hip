@@ -75,7 +75,19 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
     float kv[kIdxDim];
     float ks = 0.0f;
     if (row >= 0) {
-        for (int i = 0; i < kIdxDim; i++) kv[i] = load_elem(kc.data, dtype, row * kIdxDim + i);
+        if (dtype == DSA_F32) {   // 16-byte loads (a row is 512 bytes)
+            const f32x4* kr = (const f32x4*)((const float*)kc.data + row * kIdxDim);
+#pragma unroll
+            for (int i = 0; i < kIdxDim / 4; i++) {
+                const f32x4 v = kr[i];
+                kv[4 * i] = v[0];
+                kv[4 * i + 1] = v[1];
+                kv[4 * i + 2] = v[2];
+                kv[4 * i + 3] = v[3];
+            }
+        } else {
+            for (int i = 0; i < kIdxDim; i++) kv[i] = load_elem(kc.data, dtype, row * kIdxDim + i);
+        }
         ks = kc.scale ? kc.scale[row] : 1.0f;
     } else {
         for (int i = 0; i < kIdxDim; i++) kv[i] = 0.0f;
@@ -83,7 +95,14 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
     float total = 0.0f;
     for (int j = 0; j < H; j++) {
         float dot = 0.0f;
-        for (int i = 0; i < kIdxDim; i++) dot = fmaf(qs[j * kIdxDim + i], kv[i], dot);
+#pragma unroll
+        for (int i = 0; i < kIdxDim; i += 4) {   // the query row in 16-byte LDS reads, same order of FMAs
+            const f32x4 qv = *(const f32x4*)&qs[j * kIdxDim + i];
+            dot = fmaf(qv[0], kv[i], dot);
+            dot = fmaf(qv[1], kv[i + 1], dot);
+            dot = fmaf(qv[2], kv[i + 2], dot);
+            dot = fmaf(qv[3], kv[i + 3], dot);
+        }
         total = fmaf(wsh[j], relu_bits(dot), total);
     }
     scores[(int64_t)t * ld + s] = scale * ks * total;
