@@ -16,8 +16,9 @@
 //                  (v_mfma_f32_32x32x16_bf16).  MFMA-bound.
 //   * fp8 prefill: the same streamed structure with the fp8 MFMA, for fp8 batches with more than
 //                  eight queries per sequence.
-//   * generic:     any dtype / head count, one thread per (query, key); used for fp32 inputs and
-//                  shapes the MFMA kernels do not cover.
+//   * f32, up to 32 heads: v_mfma_f32_32x32x2_f32 with (token, head) pairs as the 32 MFMA rows.
+//   * generic:     any dtype / head count, one thread per (query, key); used for the shapes the
+//                  MFMA kernels do not cover (f32 with more than 32 heads, other head counts).
 // The ReLU-weight-sum epilogue runs on the MFMA accumulators in registers: the 32x32 accumulator
 // layout gives every lane 16 head rows of one key column, so the head sum is 16 in-register FMAs
 // per tile plus one cross-half shuffle.
@@ -106,6 +107,129 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
         total = fmaf(wsh[j], relu_bits(dot), total);
     }
     scores[(int64_t)t * ld + s] = scale * ks * total;
+}
+
+// ---------------------------------------------------------------------------------------------
+// f32 path for up to 32 heads (H dividing 32): v_mfma_f32_32x32x2_f32.
+//
+// A 32-row MFMA block holds 32 / H consecutive query tokens of one sequence times their H heads:
+// row r is (token r / H, head r % H), so the block's query rows are 32 consecutive rows of q
+// ([T, H, 128] flattened).  The 32 columns are keys.  In step s (0..63) the two k-slots carry dims
+// s and 64 + s: lane (g, c) holds dims [64g, 64g + 64) of query row c and of key c, both read with
+// 16-byte loads.  Accumulator register i of lane (g, c) is row 8(i/4) + 4g + i%4 against key c: for
+// H <= 4 all rows of a token lie in one lane, for H >= 8 they are split over lanes c and c + 32 (one
+// cross-half add).  A workgroup takes one row block and 256 consecutive keys (two 32-key tiles per
+// wave, both loaded before the first MFMA).
+constexpr int kF32Waves = 4;
+constexpr int kF32Tiles = 2;                           // 32-key tiles per wave
+constexpr int kF32Chunk = kF32Waves * kF32Tiles * 32;  // keys per workgroup
+
+template <int H>
+__global__ __launch_bounds__(kF32Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_f32_mfma_kernel(
+    const float* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
+    static_assert(H >= 1 && H <= 32 && 32 % H == 0, "heads must divide 32");
+    constexpr int QR = 32 / H;   // tokens per row block
+    __shared__ __attribute__((aligned(16))) float wsh[32];   // w' = w * q_scale of the block's 32 rows
+    __shared__ int nsh[QR];                                  // visible positions of the block's tokens
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    int qb = bv.cu_q[b], qe = bv.cu_q[b + 1];
+    qb = max(0, min(qb, bv.T));
+    qe = max(qb, min(qe, bv.T));
+    const int t0 = qb + QR * blockIdx.x;
+    if (t0 >= qe) return;
+    const int nq = min(QR, qe - t0);
+    if (tid < 32) {
+        const int tl = tid / H;
+        const int64_t r = (int64_t)min(t0 + tl, qe - 1) * H + tid % H;
+        const float ws = q_scale ? q_scale[r] : 1.0f;
+        wsh[tid] = tl < nq ? w[r] * ws : 0.0f;
+    }
+    if (tid < QR) {
+        int n = tid < nq ? min(bv.q_len[t0 + tid], bv.max_len) : 0;
+        if (n <= skip_le) n = 0;
+        nsh[tid] = max(n, 0);
+    }
+    __syncthreads();
+    const int64_t s_lo = (int64_t)blockIdx.y * kF32Chunk;
+    if (mask) {   // this block's positions past n (the last block also takes [grid end, ld))
+        const int64_t s_hi = blockIdx.y + 1 == gridDim.y ? ld : min(ld, s_lo + kF32Chunk);
+        for (int u = 0; u < nq; u++)
+            write_masked(scores + (int64_t)(t0 + u) * ld, max(s_lo, (int64_t)nsh[u]), s_hi, tid, kF32Waves * 64);
+    }
+    int nmax = 0;
+    for (int u = 0; u < nq; u++) nmax = max(nmax, nsh[u]);
+    const int64_t key0 = s_lo + (int64_t)wave * kF32Tiles * 32;
+    if (key0 >= nmax) return;
+
+    // query rows: row c of the block, dims [64g, 64g + 64); rows of tokens past the batch read a valid
+    // row and are never stored
+    float qv[64];
+    {
+        const int64_t r = min((int64_t)t0 * H + c, (int64_t)qe * H - 1);
+        const f32x4* src = (const f32x4*)(q + r * kIdxDim + 64 * g);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const f32x4 v = src[i];
+            qv[4 * i] = v[0];
+            qv[4 * i + 1] = v[1];
+            qv[4 * i + 2] = v[2];
+            qv[4 * i + 3] = v[3];
+        }
+    }
+    // keys of both tiles (positions past the context read its last key; an invalid page is a zero row)
+    float kv[kF32Tiles][64];
+    float ks[kF32Tiles];
+#pragma unroll
+    for (int tt = 0; tt < kF32Tiles; tt++) {
+        const int64_t s = min(key0 + 32 * tt + c, (int64_t)nmax - 1);
+        const int64_t row = cache_row(kc, b, s);
+        const bool ok = row >= 0;
+        const f32x4* src = (const f32x4*)((const float*)kc.data + (ok ? row : 0) * kIdxDim + 64 * g);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const f32x4 v = src[i];
+            kv[tt][4 * i] = ok ? v[0] : 0.0f;
+            kv[tt][4 * i + 1] = ok ? v[1] : 0.0f;
+            kv[tt][4 * i + 2] = ok ? v[2] : 0.0f;
+            kv[tt][4 * i + 3] = ok ? v[3] : 0.0f;
+        }
+        ks[tt] = ok ? (kc.scale ? kc.scale[row] : 1.0f) : 0.0f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < kF32Tiles; tt++) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int st = 0; st < 64; st++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[st], kv[tt][st], acc, 0, 0, 0);
+        // weighted ReLU head sums: dense index du of the lane's tokens
+        constexpr int NU = H <= 4 ? 16 / H : 32 / H;   // tokens per lane
+        float tot[NU];
+#pragma unroll
+        for (int u = 0; u < NU; u++) tot[u] = 0.0f;
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const f32x4 wv = *(const f32x4*)&wsh[8 * a + 4 * g];   // rows 8a + 4g + [0, 4)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int du = H <= 4 ? a * (4 / H) + e / H : (8 * a) / H;
+                tot[du] = fmaf(wv[e], relu_bits(acc[4 * a + e]), tot[du]);
+            }
+        }
+        if constexpr (H >= 8) {
+#pragma unroll
+            for (int u = 0; u < NU; u++) tot[u] += __shfl_xor(tot[u], 32, 64);
+        }
+        const int64_t s = key0 + 32 * tt + c;
+#pragma unroll
+        for (int u = 0; u < NU; u++) {
+            // token of dense index u: H <= 4: row 8a + 4g + e with u = a (4/H) + e/H; H >= 8: 8a/H = u
+            const int tl = H <= 4 ? (8 * (u / (4 / H))) / H + (4 * g) / H + (u % (4 / H)) : u;
+            if ((H <= 4 || g == 0) && tl < nq && s < nsh[tl])
+                scores[(int64_t)(t0 + tl) * ld + s] = scale * ks[tt] * tot[u];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -929,6 +1053,20 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
         else
             indexer_bf16_prefill_kernel<2><<<grid, kPreWaves * 64, 0, st>>>(
                 (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
+        return hipGetLastError();
+    }
+    if (dtype == DSA_F32 && H >= 1 && H <= 32 && 32 % H == 0) {
+        const int qr = 32 / H;
+        dim3 grid((bv.max_q + qr - 1) / qr, (bv.max_len + kF32Chunk - 1) / kF32Chunk, bv.B);
+        const float* qf = (const float*)q;
+        switch (H) {
+            case 1: indexer_f32_mfma_kernel<1><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            case 2: indexer_f32_mfma_kernel<2><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            case 4: indexer_f32_mfma_kernel<4><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            case 8: indexer_f32_mfma_kernel<8><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            case 16: indexer_f32_mfma_kernel<16><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            default: indexer_f32_mfma_kernel<32><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+        }
         return hipGetLastError();
     }
     const size_t shm = (size_t)H * (kIdxDim + 1) * sizeof(float);

@@ -168,7 +168,10 @@ SMALL = [
     ("decode-fp8-ragged", [1, 31, 32, 33, 64, 65, 100, 257, 1000, 2049, 4097], [1] * 11, 64, synth.FP8, 64, 128, True),
     ("mtp-fp8-h32", [70, 129, 3000], [2, 2, 2], 32, synth.FP8, 64, 64, False),
     ("decode-bf16-contig", [500, 1025], [1, 1], 64, synth.BF16, 128, 48, False),
-    ("decode-f32-generic", [600, 90], [3, 1], 8, synth.F32, 50, 8, True),
+    ("decode-f32-h8-mfma", [600, 90], [3, 1], 8, synth.F32, 50, 8, True),
+    ("decode-f32-h64-generic", [600, 90], [3, 1], 64, synth.F32, 50, 8, True),
+    # f32 with (token, head) MFMA rows: 16 heads, causal prefill over two sequences, 64-token pages
+    ("prefill-f32-h16-paged", [333, 70], [333, 70], 16, synth.F32, 100, 16, True),
     # bf16 prefill over several sequences, queries at the end of a longer context, 64-token pages
     ("prefill-bf16-3seq-paged", [200, 777, 64], [200, 300, 64], 64, synth.BF16, 128, 16, True),
     # 16-token pages: the bf16 kernel for any cache layout
@@ -230,12 +233,13 @@ def test_paged_equals_contiguous_bitwise():
     assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dt,nq", [(synth.BF16, [300, 1]), (synth.FP8, [1, 1]), (synth.FP8, [300, 1])],
-                         ids=["bf16-prefill", "fp8-decode", "fp8-prefill-stream"])
-def test_indexer_out_of_range_pages_read_as_zero_rows(dt, nq):
+@pytest.mark.parametrize("dt,nq,hi", [(synth.BF16, [300, 1], 64), (synth.FP8, [1, 1], 64), (synth.FP8, [300, 1], 64),
+                                      (synth.F32, [300, 1], 4), (synth.F32, [2, 1], 64)],
+                         ids=["bf16-prefill", "fp8-decode", "fp8-prefill-stream", "f32-h4-mfma", "f32-h64-generic"])
+def test_indexer_out_of_range_pages_read_as_zero_rows(dt, nq, hi):
     """Page numbers outside [0, num_pages) read as all-zero key rows: those tokens score exactly 0
     (ReLU(0) = 0) and every other score is unchanged, bit for bit."""
-    spec = synth.Spec(f"badpage-{dt}-{nq[0]}", ctx=[700, 300], nq=nq, idx_heads=64, idx_dtype=dt, topk=64,
+    spec = synth.Spec(f"badpage-{dt}-{nq[0]}-h{hi}", ctx=[700, 300], nq=nq, idx_heads=hi, idx_dtype=dt, topk=64,
                       paged=True, seed=13)
     p = synth.build(spec)
     dp = to_device(p)
