@@ -16,9 +16,10 @@
 //                  (v_mfma_f32_32x32x16_bf16).  MFMA-bound.
 //   * fp8 prefill: the same streamed structure with the fp8 MFMA, for fp8 batches with more than
 //                  eight queries per sequence.
-//   * f32, up to 32 heads: v_mfma_f32_32x32x2_f32 with (token, head) pairs as the 32 MFMA rows.
+//   * up to 32 heads, any dtype: (token, head) pairs as the 32 MFMA rows (f32, bf16 or fp8 MFMA);
+//                  f32 inputs, and bf16 / fp8 shapes the kernels above do not take.
 //   * generic:     any dtype / head count, one thread per (query, key); used for the shapes the
-//                  MFMA kernels do not cover (f32 with more than 32 heads, other head counts).
+//                  MFMA kernels do not cover (more than 32 heads that are not 32 or 64).
 // The ReLU-weight-sum epilogue runs on the MFMA accumulators in registers: the 32x32 accumulator
 // layout gives every lane 16 head rows of one key column, so the head sum is 16 in-register FMAs
 // per tile plus one cross-half shuffle.
@@ -110,23 +111,78 @@ __global__ __launch_bounds__(kGenBlock) void indexer_generic_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// f32 path for up to 32 heads (H dividing 32): v_mfma_f32_32x32x2_f32.
+// Up to 32 heads (H dividing 32), any dtype: (token, head) pairs as the MFMA rows.
 //
 // A 32-row MFMA block holds 32 / H consecutive query tokens of one sequence times their H heads:
 // row r is (token r / H, head r % H), so the block's query rows are 32 consecutive rows of q
-// ([T, H, 128] flattened).  The 32 columns are keys.  In step s (0..63) the two k-slots carry dims
-// s and 64 + s: lane (g, c) holds dims [64g, 64g + 64) of query row c and of key c, both read with
-// 16-byte loads.  Accumulator register i of lane (g, c) is row 8(i/4) + 4g + i%4 against key c: for
-// H <= 4 all rows of a token lie in one lane, for H >= 8 they are split over lanes c and c + 32 (one
-// cross-half add).  A workgroup takes one row block and 256 consecutive keys (two 32-key tiles per
-// wave, both loaded before the first MFMA).
-constexpr int kF32Waves = 4;
-constexpr int kF32Tiles = 2;                           // 32-key tiles per wave
-constexpr int kF32Chunk = kF32Waves * kF32Tiles * 32;  // keys per workgroup
+// ([T, H, 128] flattened).  The 32 columns are keys.  Lane (g, c) holds dims [64g, 64g + 64) of
+// query row c and of key c, read with 16-byte loads, and the k-slots of each MFMA step map onto
+// those dims the same way for both operands:
+//   f32  v_mfma_f32_32x32x2_f32, 64 steps: step s carries dims s and 64 + s;
+//   bf16 v_mfma_f32_32x32x16_bf16, 8 steps: half g carries dims 64g + 8s + [0, 8);
+//   fp8  v_mfma_scale_f32_32x32x64_f8f6f4, 2 steps: half g carries dims 64g + 32s + [0, 32).
+// Accumulator register i of lane (g, c) is row 8(i/4) + 4g + i%4 against key c: for H <= 4 all rows
+// of a token lie in one lane, for H >= 8 they are split over lanes c and c + 32 (one cross-half add).
+// A workgroup takes one row block and 256 consecutive keys (two 32-key tiles per wave, both loaded
+// before the first MFMA).  Used for f32 inputs and for bf16 / fp8 batches the specialised kernels
+// above do not take (fewer than 32 heads, fp8 caches without key scales or with pages of fewer
+// than 64 tokens).
+constexpr int kRowWaves = 4;
+constexpr int kRowTiles = 2;                           // 32-key tiles per wave
+constexpr int kRowChunk = kRowWaves * kRowTiles * 32;  // keys per workgroup
 
-template <int H>
-__global__ __launch_bounds__(kF32Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_f32_mfma_kernel(
-    const float* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+// One lane's 64 dims of a query or key row in the operand form of dtype DT.
+template <int DT> struct RowOperand;
+template <> struct RowOperand<DSA_F32> {
+    float v[64];
+    __device__ __forceinline__ void load(const void* base, int64_t row, int g, bool ok) {
+        const f32x4* src = (const f32x4*)((const float*)base + row * kIdxDim + 64 * g);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const f32x4 x = src[i];
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[4 * i + e] = ok ? x[e] : 0.0f;
+        }
+    }
+};
+template <> struct RowOperand<DSA_BF16> {
+    bf16x8 v[8];
+    __device__ __forceinline__ void load(const void* base, int64_t row, int g, bool ok) {
+        const bf16x8* src = (const bf16x8*)((const uint16_t*)base + row * kIdxDim + 64 * g);
+        const bf16x8 zero = {};
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = ok ? src[i] : zero;
+    }
+};
+template <> struct RowOperand<DSA_FP8_E4M3> {
+    i32x8 v[2];
+    __device__ __forceinline__ void load(const void* base, int64_t row, int g, bool ok) {
+        const i32x8* src = (const i32x8*)((const uint8_t*)base + row * kIdxDim + 64 * g);
+        const i32x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+        v[0] = ok ? src[0] : zero;
+        v[1] = ok ? src[1] : zero;
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ f32x16 row_dots(const RowOperand<DT>& qo, const RowOperand<DT>& ko) {
+    f32x16 acc = {};
+    if constexpr (DT == DSA_F32) {
+#pragma unroll
+        for (int st = 0; st < 64; st++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qo.v[st], ko.v[st], acc, 0, 0, 0);
+    } else if constexpr (DT == DSA_BF16) {
+#pragma unroll
+        for (int st = 0; st < 8; st++) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qo.v[st], ko.v[st], acc, 0, 0, 0);
+    } else {
+        acc = mfma_fp8(qo.v[0], ko.v[0], acc);
+        acc = mfma_fp8(qo.v[1], ko.v[1], acc);
+    }
+    return acc;
+}
+
+template <int H, int DT>
+__global__ __launch_bounds__(kRowWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_rows_mfma_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
     static_assert(H >= 1 && H <= 32 && 32 % H == 0, "heads must divide 32");
     constexpr int QR = 32 / H;   // tokens per row block
@@ -153,56 +209,34 @@ __global__ __launch_bounds__(kF32Waves * 64) __attribute__((amdgpu_waves_per_eu(
         nsh[tid] = max(n, 0);
     }
     __syncthreads();
-    const int64_t s_lo = (int64_t)blockIdx.y * kF32Chunk;
+    const int64_t s_lo = (int64_t)blockIdx.y * kRowChunk;
     if (mask) {   // this block's positions past n (the last block also takes [grid end, ld))
-        const int64_t s_hi = blockIdx.y + 1 == gridDim.y ? ld : min(ld, s_lo + kF32Chunk);
+        const int64_t s_hi = blockIdx.y + 1 == gridDim.y ? ld : min(ld, s_lo + kRowChunk);
         for (int u = 0; u < nq; u++)
-            write_masked(scores + (int64_t)(t0 + u) * ld, max(s_lo, (int64_t)nsh[u]), s_hi, tid, kF32Waves * 64);
+            write_masked(scores + (int64_t)(t0 + u) * ld, max(s_lo, (int64_t)nsh[u]), s_hi, tid, kRowWaves * 64);
     }
     int nmax = 0;
     for (int u = 0; u < nq; u++) nmax = max(nmax, nsh[u]);
-    const int64_t key0 = s_lo + (int64_t)wave * kF32Tiles * 32;
+    const int64_t key0 = s_lo + (int64_t)wave * kRowTiles * 32;
     if (key0 >= nmax) return;
 
-    // query rows: row c of the block, dims [64g, 64g + 64); rows of tokens past the batch read a valid
-    // row and are never stored
-    float qv[64];
-    {
-        const int64_t r = min((int64_t)t0 * H + c, (int64_t)qe * H - 1);
-        const f32x4* src = (const f32x4*)(q + r * kIdxDim + 64 * g);
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const f32x4 v = src[i];
-            qv[4 * i] = v[0];
-            qv[4 * i + 1] = v[1];
-            qv[4 * i + 2] = v[2];
-            qv[4 * i + 3] = v[3];
-        }
-    }
+    // query rows: row c of the block; rows of tokens past the batch read a valid row and are never stored
+    RowOperand<DT> qo;
+    qo.load(q, min((int64_t)t0 * H + c, (int64_t)qe * H - 1), g, true);
     // keys of both tiles (positions past the context read its last key; an invalid page is a zero row)
-    float kv[kF32Tiles][64];
-    float ks[kF32Tiles];
+    RowOperand<DT> ko[kRowTiles];
+    float ks[kRowTiles];
 #pragma unroll
-    for (int tt = 0; tt < kF32Tiles; tt++) {
+    for (int tt = 0; tt < kRowTiles; tt++) {
         const int64_t s = min(key0 + 32 * tt + c, (int64_t)nmax - 1);
         const int64_t row = cache_row(kc, b, s);
         const bool ok = row >= 0;
-        const f32x4* src = (const f32x4*)((const float*)kc.data + (ok ? row : 0) * kIdxDim + 64 * g);
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const f32x4 v = src[i];
-            kv[tt][4 * i] = ok ? v[0] : 0.0f;
-            kv[tt][4 * i + 1] = ok ? v[1] : 0.0f;
-            kv[tt][4 * i + 2] = ok ? v[2] : 0.0f;
-            kv[tt][4 * i + 3] = ok ? v[3] : 0.0f;
-        }
+        ko[tt].load(kc.data, ok ? row : 0, g, ok);
         ks[tt] = ok ? (kc.scale ? kc.scale[row] : 1.0f) : 0.0f;
     }
 #pragma unroll
-    for (int tt = 0; tt < kF32Tiles; tt++) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int st = 0; st < 64; st++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[st], kv[tt][st], acc, 0, 0, 0);
+    for (int tt = 0; tt < kRowTiles; tt++) {
+        const f32x16 acc = row_dots<DT>(qo, ko[tt]);
         // weighted ReLU head sums: dense index du of the lane's tokens
         constexpr int NU = H <= 4 ? 16 / H : 32 / H;   // tokens per lane
         float tot[NU];
@@ -1055,18 +1089,23 @@ hipError_t launch_indexer(const void* q, int dtype, const float* q_scale, const 
                 (const uint16_t*)q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask);
         return hipGetLastError();
     }
-    if (dtype == DSA_F32 && H >= 1 && H <= 32 && 32 % H == 0) {
+    if ((dtype == DSA_F32 || dtype == DSA_BF16 || dtype == DSA_FP8_E4M3) && H >= 1 && H <= 32 && 32 % H == 0) {
         const int qr = 32 / H;
-        dim3 grid((bv.max_q + qr - 1) / qr, (bv.max_len + kF32Chunk - 1) / kF32Chunk, bv.B);
-        const float* qf = (const float*)q;
-        switch (H) {
-            case 1: indexer_f32_mfma_kernel<1><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-            case 2: indexer_f32_mfma_kernel<2><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-            case 4: indexer_f32_mfma_kernel<4><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-            case 8: indexer_f32_mfma_kernel<8><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-            case 16: indexer_f32_mfma_kernel<16><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-            default: indexer_f32_mfma_kernel<32><<<grid, kF32Waves * 64, 0, st>>>(qf, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
-        }
+        dim3 grid((bv.max_q + qr - 1) / qr, (bv.max_len + kRowChunk - 1) / kRowChunk, bv.B);
+        auto go = [&](auto dt) {
+            constexpr int DT = decltype(dt)::value;
+            switch (H) {
+                case 1: indexer_rows_mfma_kernel<1, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+                case 2: indexer_rows_mfma_kernel<2, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+                case 4: indexer_rows_mfma_kernel<4, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+                case 8: indexer_rows_mfma_kernel<8, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+                case 16: indexer_rows_mfma_kernel<16, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+                default: indexer_rows_mfma_kernel<32, DT><<<grid, kRowWaves * 64, 0, st>>>(q, q_scale, w, kc, bv, scale, scores, ld, skip_le, mask); break;
+            }
+        };
+        if (dtype == DSA_F32) go(std::integral_constant<int, DSA_F32>{});
+        else if (dtype == DSA_BF16) go(std::integral_constant<int, DSA_BF16>{});
+        else go(std::integral_constant<int, DSA_FP8_E4M3>{});
         return hipGetLastError();
     }
     const size_t shm = (size_t)H * (kIdxDim + 1) * sizeof(float);

@@ -14,9 +14,10 @@ Launch paths (the dispatch in csrc/indexer.hip): fp8 with 32 or 64 heads and at 
 sequence -> the fp8 decode kernel (one query per pass when max_q == 1, two otherwise); bf16 in a
 contiguous cache or 64-token pages -> the DMA-streamed kernel; bf16 in 16-token pages -> the
 four-query kernel; fp8 with more than 8 queries per sequence in a contiguous cache or 64-token pages
--> the fp8 streamed kernel; f32 with 1, 2, 4, 8, 16 or 32 heads -> the f32 MFMA kernel ((token, head)
-rows, contiguous and paged, causal and ragged, tails of a 256-key chunk); f32 with more heads and
-other head counts -> the generic kernel.  The 32-head streamed
+-> the fp8 streamed kernel; 1, 2, 4, 8, 16 or 32 heads in f32, and the bf16 / fp8 shapes none of the
+kernels above takes (fewer than 32 heads; fp8 prefill in 16-token pages) -> the (token, head)-row MFMA
+kernel (contiguous and paged, causal and ragged, tails of a 256-key chunk); f32 with 64 heads and fp8
+with 48 -> the generic kernel.  The 32-head streamed
 kernel (operands read from LDS a few MFMAs ahead, two workgroups per CU) has a paged and a ragged
 contiguous case.
 """
@@ -52,6 +53,11 @@ CASES = [
     ("f32-mfma-h2-page16", [130, 9], [65, 9], 2, F32, True, 16),
     ("f32-mfma-h16-paged", [600, 257], [9, 1], 16, F32, True, 64),
     ("f32-mfma-h32-contig", [333, 64], [33, 2], 32, F32, False, 64),
+    ("bf16-rows-h16-paged", [300, 77], [300, 5], 16, BF16, True, 64),
+    ("bf16-rows-h4-page16", [130, 9], [65, 9], 4, BF16, True, 16),
+    ("fp8-rows-h8-decode", [1000, 4097, 33], [1, 1, 1], 8, FP8, False, 64),
+    ("fp8-rows-h16-prefill-paged", [300, 130], [300, 9], 16, FP8, True, 64),
+    ("fp8-rows-h32-prefill-page16", [200, 50], [200, 3], 32, FP8, True, 16),
     ("fp8-stream-12q-h64", [500, 77], [12, 2], 64, FP8, False, 64),
     ("fp8-stream-prefill-h32-paged64", [300, 130], [300, 9], 32, FP8, True, 64),
     ("fp8-generic-h48", [700, 35], [1, 1], 48, FP8, True, 64),

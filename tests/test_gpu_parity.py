@@ -172,6 +172,9 @@ SMALL = [
     ("decode-f32-h64-generic", [600, 90], [3, 1], 64, synth.F32, 50, 8, True),
     # f32 with (token, head) MFMA rows: 16 heads, causal prefill over two sequences, 64-token pages
     ("prefill-f32-h16-paged", [333, 70], [333, 70], 16, synth.F32, 100, 16, True),
+    # bf16 / fp8 with fewer than 32 indexer heads: the same (token, head)-row kernel with their MFMAs
+    ("prefill-bf16-h8-rows", [333], [333], 8, synth.BF16, 100, 16, False),
+    ("decode-fp8-h16-rows-paged", [600, 90, 3000], [1, 1, 1], 16, synth.FP8, 50, 8, True),
     # bf16 prefill over several sequences, queries at the end of a longer context, 64-token pages
     ("prefill-bf16-3seq-paged", [200, 777, 64], [200, 300, 64], 64, synth.BF16, 128, 16, True),
     # 16-token pages: the bf16 kernel for any cache layout
