@@ -84,12 +84,13 @@ typedef struct {
 /* A batch of query tokens grouped by sequence (queries of a sequence are consecutive). */
 typedef struct {
     int32_t num_queries;         /* T */
-    int32_t num_seqs;            /* B */
+    int32_t num_seqs;            /* B, 1 .. 65535 */
     const int32_t* cu_q;         /* device [B+1]: queries of sequence b are cu_q[b] .. cu_q[b+1]-1 */
     const int32_t* q_seq;        /* device [T]: sequence of each query */
     const int32_t* q_len;        /* device [T]: n_t, query t sees its sequence's tokens 0..n_t-1
                                     (causal; a token sees itself, so in prefill n_t = position + 1) */
-    int32_t max_len;             /* host: an upper bound of every n_t (sizes grids and score rows) */
+    int32_t max_len;             /* host: an upper bound of every n_t (sizes grids and score rows),
+                                    at most 65535 * 256 = 16776960 */
     int32_t max_q;               /* host: an upper bound of the queries of one sequence */
 } dsa_batch;
 

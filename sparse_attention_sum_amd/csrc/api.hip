@@ -35,10 +35,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t score_ld(const dsa_batch* b) { return ((int64_t)b->max_len + 63) & ~(int64_t)63; }
 
+constexpr int kMaxSeqs = 65535;
+constexpr int kMaxLen = 65535 * 256;
+
 dsa_status check_batch(const dsa_batch* b) {
     if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
     if (b->num_queries < 0 || b->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "batch: num_queries < 0 or num_seqs < 1");
     if (b->max_len < 0) return fail(DSA_ERR_INVALID_ARG, "batch: max_len < 0");
+    // launch grids take one sequence per row of their second or third dimension, and the indexer's
+    // 256-position blocks of a row along a second dimension (at most 65535 each)
+    if (b->num_seqs > kMaxSeqs) return fail(DSA_ERR_INVALID_ARG, "batch: num_seqs %d > %d", b->num_seqs, kMaxSeqs);
+    if (b->max_len > kMaxLen) return fail(DSA_ERR_INVALID_ARG, "batch: max_len %d > %d", b->max_len, kMaxLen);
     if (b->num_queries > 0) {
         if (!b->cu_q || !b->q_seq || !b->q_len) return fail(DSA_ERR_INVALID_ARG, "batch: cu_q / q_seq / q_len is NULL");
         if (b->max_q < 1 || b->max_q > b->num_queries)

@@ -74,6 +74,14 @@ def test_indexer_validation(lib):
     assert _idx(lib, cache=_cache(pt=FAKE, pt_stride=2, page=0)) == dsa.DSA_ERR_INVALID_ARG
     assert _idx(lib, batch=_batch(max_q=0)) == dsa.DSA_ERR_INVALID_ARG
     assert _idx(lib, batch=_batch(B=0)) == dsa.DSA_ERR_INVALID_ARG
+    # launch-grid limits, rejected by the batch check itself (the message names the field)
+    big = _cache(rows=65536 * 100)
+    assert _idx(lib, batch=_batch(B=65536), cache=big) == dsa.DSA_ERR_INVALID_ARG
+    assert b"num_seqs 65536 > 65535" in lib.dsa_last_error()
+    assert _idx(lib, batch=_batch(B=65535), cache=big, q=None) == dsa.DSA_ERR_INVALID_ARG   # the limit itself passes
+    assert b"q or weights" in lib.dsa_last_error()
+    assert _idx(lib, batch=_batch(max_len=65535 * 256 + 1)) == dsa.DSA_ERR_INVALID_ARG
+    assert b"max_len 16776961 > 16776960" in lib.dsa_last_error()
     bad = dsa._Batch(4, 1, None, FAKE, FAKE, 100, 4)
     assert _idx(lib, batch=bad) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_indexer_scores(FAKE, 2, None, FAKE, 64, 128, None, ctypes.byref(_batch()), 1.0, FAKE, 128,
