@@ -197,6 +197,25 @@ def test_long_rows_two_pass_topk_forward():
     rows = list(range(spec.T))
     check_problem(dp, rows_idx=[0, 2, 3], rows_topk=rows, rows_mla=[0, 2, 3, 5], label=spec.name)
 
+LARGE_K = [
+    # name, ctx, nq, k: k past one sparse-MLA split's 2048 slots (64 splits, the runtime combine), up to
+    # the largest k the boundary takes; a row of 70000 keys selects 65536 (single-pass top-k whose
+    # candidates do not fit LDS: the row is re-read from global memory on each pass), one of 30000
+    # keys selects all of them
+    ("largek-4096", [10000, 3000, 5000], [1, 1, 2], 4096),
+    ("largek-65536", [70000, 30000], [1, 1], 65536),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_K, ids=[c[0] for c in LARGE_K])
+def test_large_k_forward(case):
+    name, ctx, nq, k = case
+    spec = synth.Spec(name, ctx=ctx, nq=nq, idx_dtype=synth.FP8, topk=k, mla_heads=128, paged=True, seed=17)
+    dp = device_problem(spec)
+    rows = list(range(spec.T))
+    check_problem(dp, rows_idx=rows, rows_topk=rows, rows_mla=rows, label=spec.name)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_workloads_all_rows(case):
     name, ctx, nq, hi, dt, k, h, paged = case[:8]
