@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
 // workgroup per CU over the batch's sequences.
 bool plan_slices(const BatchView& bv, int k, int qg, int& ns, int& slen) {
     if (k <= 0 || bv.T <= 0 || bv.max_len <= k) return false;
-    if (bv.max_len * qg <= kCap) {
+    if ((int64_t)bv.max_len * qg <= kCap) {
         // the row fits one slice; when one workgroup per sequence would leave CUs idle, it is split
         // into slices of at least kFuSplitMin positions (measured: 64 x 32768 as four slices of 8192,
         // indexer + top-k 81 us against 87 unfused and 150 as one slice; slices of 4096 lost to the
@@ -220,7 +220,7 @@ bool indexer_topk_rows_exceed_slice(const BatchView& bv) { return (int64_t)bv.ma
 
 size_t indexer_topk_workspace_bound(const BatchView& bv, int k) {
     if (k <= 0 || bv.T <= 0) return 0;
-    if (bv.max_len * bv.max_q <= kCap && bv.max_len < 2 * kFuSplitMin) return 0;   // one slice: no candidates
+    if ((int64_t)bv.max_len * bv.max_q <= kCap && bv.max_len < 2 * kFuSplitMin) return 0;   // one slice: no candidates
     return slices_bytes(bv.T, min(kTkWaves, kCandCap / max(k, 1)), k);
 }
 

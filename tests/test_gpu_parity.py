@@ -216,6 +216,62 @@ def test_large_k_forward(case):
     check_problem(dp, rows_idx=rows, rows_topk=rows, rows_mla=rows, label=spec.name)
 
 
+def test_longest_context_the_boundary_takes():
+    """One query over 65535 * 256 = 16776960 positions, the largest max_len the batch check accepts
+    (the indexer's 256-position blocks then fill a grid dimension): the fp8 indexer over a 2.1 GB key
+    cache, the single-pass top-k over a 67 MB score row (its slices would not fit LDS, so no two-pass
+    split), and sparse MLA over the 2048 selected rows of a 19 GB latent cache.  Inputs are drawn on
+    the device; the checks sample: the indexer on 65536 random positions against the oracle, the
+    top-k set on the GPU's own scores bit for bit, the attention on the selected rows, and
+    dsa_forward equal to the chain bit for bit."""
+    ctx, k, scale = 65535 * 256, 2048, 1.0 / 24.0
+    d = synth.build_decode_on_device(ctx, batch=1, seed=5)
+    b = dsa.Batch(cu_q=d["cu_q"], q_seq=d["q_seq"], q_len=d["q_len"], max_len=ctx, max_q=1)
+    kc = dsa.Cache(d["k_idx"], d["k_idx_scale"], seq_stride=ctx)
+    lc = dsa.Cache(d["latent"], seq_stride=ctx)
+    ld = dsa.score_ld(b)
+    scores = dsa.dsa_indexer_scores(d["q_idx"], d["q_idx_scale"], d["w"], kc, b, scale=1.0, ld=ld)
+    idx = dsa.dsa_topk(scores, ld, b, k)
+    out, lse = dsa.dsa_sparse_mla(d["q_mla"], lc, b, idx, scale)
+    torch.cuda.synchronize()
+    log(f"max context {ctx}: GPU chain done")
+    g = scores[0, :ctx].double().cpu().numpy()
+    assert np.all(np.isneginf(scores[0, ctx:].cpu().numpy()))
+    # indexer on sampled positions: the sampled key rows as one sequence of their own
+    pos = np.sort(np.random.default_rng(3).choice(ctx, size=65536, replace=False)).astype(np.int64)
+    kq = d["q_idx"].view(torch.uint8).cpu().numpy()
+    qs, wt = d["q_idx_scale"].cpu().numpy(), d["w"].cpu().numpy()
+    pos_t = torch.from_numpy(pos).cuda()
+    krows = d["k_idx"][pos_t].view(torch.uint8).cpu().numpy()
+    ksc = d["k_idx_scale"][pos_t].cpu().numpy()
+    one = dict(q_seq=np.zeros(1, np.int32), q_len=np.array([len(pos)], np.int32), seq_stride=len(pos), nthreads=NTHREADS)
+    ref = oracle.indexer(kq, "fp8", qs, wt, krows, "fp8", ksc, **one)[0, :len(pos)]
+    A = oracle.indexer(kq & np.uint8(0x7F), "fp8", qs, np.abs(wt), krows & np.uint8(0x7F), "fp8", ksc, **one)[0, :len(pos)]
+    err = float((np.abs(g[pos] - ref) / np.maximum(A, 1e-30)).max())
+    assert err <= 2e-2, f"indexer |err|/A {err}"
+    # top-k on the GPU's scores
+    gi = idx[0].cpu().numpy()
+    want = oracle.topk(g[None], np.array([ctx], np.int32), k, nthreads=NTHREADS)[0]
+    assert sorted(gi[gi >= 0].tolist()) == sorted(want[want >= 0].tolist()), "top-k set differs"
+    # attention on the selected rows
+    sel = torch.from_numpy(gi.astype(np.int64)).cuda()
+    lat = d["latent"][sel].view(torch.int16).cpu().numpy().view(np.uint16)
+    qm = d["q_mla"].view(torch.int16).cpu().numpy().view(np.uint16)
+    o_ref, l_ref = oracle.sparse_mla(qm, lat, np.zeros(1, np.int32), np.array([k], np.int32),
+                                     np.arange(k, dtype=np.int32)[None], seq_stride=k, softmax_scale=scale,
+                                     nthreads=NTHREADS)
+    check_mla(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "max context")
+    ind2 = torch.empty_like(idx)
+    lse2 = torch.empty_like(lse)
+    out2, _, _ = dsa.dsa_forward(d["q_idx"], d["q_idx_scale"], d["w"], kc, k, d["q_mla"], lc, b, scale,
+                                 indices_out=ind2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(ind2, idx) and torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    log(f"max context {ctx}: indexer |err|/A {err:.2e} on 65536 positions, top-k exact, MLA ok, forward == chain")
+    del d, scores, out, out2
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_workloads_all_rows(case):
     name, ctx, nq, hi, dt, k, h, paged = case[:8]
