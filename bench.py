@@ -14,6 +14,7 @@ line.  Only one GPU is supported: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -330,6 +331,8 @@ def long_context_only(args, dev):
         for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
             e0.record(stream)
             e1.record(stream)
+        gc.collect()
+        gc.disable()
         torch.cuda.synchronize()
         for e0, e1 in ev:
             flush()
@@ -337,6 +340,7 @@ def long_context_only(args, dev):
             fn()
             e1.record(stream)
         torch.cuda.synchronize()
+        gc.enable()
         return np.array([e0.elapsed_time(e1) for e0, e1 in ev]), None
 
     def prewarm(ms):
@@ -446,6 +450,10 @@ def main():
         for e0, e1 in ev:   # torch creates an event's HIP event at its first record: not inside a step
             e0.record(stream)
             e1.record(stream)
+        # no garbage-collection pass between a step's start event and its launches (a host stall
+        # there would be timed as GPU time)
+        gc.collect()
+        gc.disable()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1 in ev:
@@ -455,6 +463,7 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        gc.enable()
         ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
         return ms, wall
 
