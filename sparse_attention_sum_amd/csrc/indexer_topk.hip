@@ -32,7 +32,10 @@ __global__ __launch_bounds__(kTkBlock) void indexer_topk_kernel(const uint8_t* _
                                                                 BatchView bv, float scale, int k, TkSlices sl,
                                                                 int32_t* __restrict__ idx) {
     constexpr int H = 32 * NHS;
-    constexpr int PF = QG == 1 ? 6 : 3;    // subtiles in flight per wave (registers: 17 per subtile)
+    // subtiles in flight per wave (registers: 17 per subtile).  Four for one query: measured at decode
+    // 64 x 131072 (fused stage 223.9-225.5 us against 228.7-228.8 with six, 248-249 with eight) and in
+    // the 64 x 65536 forward (190.6-191.0 against 192.8-194.2 us); the scores are the same either way.
+    constexpr int PF = QG == 1 ? 4 : 3;
     // LDS: the scores of QG rows over the slice as keys, then the slice's page table
     extern __shared__ __align__(16) uint32_t lds[];
     __shared__ TkShared sh;
