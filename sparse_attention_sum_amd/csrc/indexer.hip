@@ -280,7 +280,7 @@ constexpr int kDecWaves = 4;
 
 
 // QG query tokens of one sequence share each key fetch (1 for plain decode, 2 for two-token
-// speculative decode).  A wave keeps PF key subtiles (32 keys each) in flight (4, or 3 for QG = 2): the loads of subtile
+// speculative decode).  A wave keeps PF = 3 key subtiles (32 keys each) in flight: the loads of subtile
 // i + PF are issued as soon as subtile i has been consumed.  The storage rows of all of the wave's
 // subtiles are looked up first (one batch of page-table loads), so a key load never waits for its
 // page lookup.  The head weights of a pass live in a per-wave LDS area (read 4 at a time where
@@ -291,7 +291,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     CacheView kc, BatchView bv, float scale, float* __restrict__ scores, int64_t ld, int skip_le, int mask) {
     constexpr int H = 32 * NHS;
-    constexpr int PF = QG == 1 ? 4 : 3;   // two queries need more registers: one subtile less
+    // three subtiles in flight, for one query or two (one query: 21.0 against 21.4-21.7 us with four at
+    // decode 64 x 8192, 61.4-61.8 against 62.8 at 64 x 32768; two queries: 82 against 86-87 us with two)
+    constexpr int PF = 3;
     constexpr int kSub = kDecKeysPerWave / 32;
     __shared__ __attribute__((aligned(16))) float wsh[kDecWaves][QG][H];   // w * q_scale, per wave
     const int b = blockIdx.y;
